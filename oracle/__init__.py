@@ -1,0 +1,18 @@
+"""Independent fp64 CPU oracle for the QK-norm + RoPE + causal / sliding-window attention path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library never calls it, and it shares no code with it.
+"""
+
+from .attention import (  # noqa: F401
+    EPS_DEFAULT,
+    ROPE_BASE_DEFAULT,
+    attention,
+    attention_layer,
+    qknorm_rope,
+    rms_norm,
+    rope_apply,
+    rope_cos_sin,
+    sssl_windows,
+    visible,
+)

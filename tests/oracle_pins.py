@@ -1,0 +1,348 @@
+"""Pin checks for the fp64 oracle, written so that a test can run them against a deliberately
+broken copy of the oracle too (``test_oracle_mutations.py``).
+
+Each check takes an object ``o`` exposing the oracle's functions (``oracle`` itself, or a
+namespace with one function replaced) and raises AssertionError when the pin fails. None of them
+re-types the oracle's formulas: they compare against closed forms, values the pages print, brute
+force with ``math.fsum``, or an independent library routine.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------------------------
+# Worked example: "Lendo uma Projeção" on "Projeção em um Subespaço de Consulta".
+# ---------------------------------------------------------------------------------------------
+
+def worked_example_inputs():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    return g
+
+
+def check_worked_example(o):
+    """Raw attention of the printed query against the three printed keys, V = identity.
+
+    Closed form: q.k = (1, 1, 0); divided by sqrt(d_k) = 2 that is (1/2, 1/2, 0); the softmax
+    weights are (sqrt(e), sqrt(e), 1) / (2 sqrt(e) + 1) and the logsumexp is ln(2 sqrt(e) + 1).
+    Rows 1 and 2 of the embedding use a zero query: weights 1/3 each, logsumexp ln 3.
+    """
+    g = worked_example_inputs()
+    assert g["sqrt_d_k"] == 2 and g["d_k"] == 4
+    T, d = 3, 4
+    q = np.zeros((1, 1, T, d))
+    q[0, 0, 0] = g["q"]
+    k = np.array(g["keys"], dtype=np.float64)[None, None]
+    v = np.eye(3)[None, None]
+    out, lse = o.attention(q, k, v, window=-1, causal=False)
+    se = math.exp(0.5)
+    w = np.array([se, se, 1.0]) / (2 * se + 1)
+    assert abs(sum(w) - 1) < 1e-15
+    np.testing.assert_allclose(out[0, 0, 0], w, rtol=0, atol=1e-15)
+    assert abs(lse[0, 0, 0] - math.log(2 * se + 1)) < 1e-15
+    np.testing.assert_allclose(out[0, 0, 1:], np.full((2, 3), 1 / 3), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0, 1:], [math.log(3)] * 2, rtol=0, atol=1e-15)
+    # Printed numbers of the closed form, to 12 digits.
+    assert abs(out[0, 0, 0, 0] - 0.383651731190) < 1e-12
+    assert abs(out[0, 0, 0, 2] - 0.232696537618) < 1e-12
+    assert abs(lse[0, 0, 0] - 1.458020087947) < 1e-12
+
+
+def check_worked_example_qknorm(o):
+    """The same example through QK-norm (no positions, so no rotation).
+
+    Closed form with eps: q_hat = q / sqrt(1/2 + eps), k1_hat = e1 / sqrt(1/4 + eps),
+    k2_hat = e3 / sqrt(1/4 + eps), k3_hat = (e2 + e4) / sqrt(1/2 + eps); the scores are
+    q_hat.k_hat / 2.
+    """
+    g = worked_example_inputs()
+    eps = 1e-6
+    q = np.array(g["q"], dtype=np.float64)
+    keys = np.array(g["keys"], dtype=np.float64)
+    qn = o.rms_norm(q, eps)
+    kn = o.rms_norm(keys, eps)
+    np.testing.assert_allclose(qn, q / math.sqrt(0.5 + eps), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(kn[0], keys[0] / math.sqrt(0.25 + eps), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(kn[2], keys[2] / math.sqrt(0.5 + eps), rtol=1e-15, atol=0)
+    s12 = 1.0 / (math.sqrt(0.5 + eps) * math.sqrt(0.25 + eps)) / 2
+    z = 2 * math.exp(s12) + 1
+    T = 3
+    qq = np.zeros((1, 1, T, 4))
+    qq[0, 0, 0] = qn
+    out, lse = o.attention(qq, kn[None, None], np.eye(3)[None, None], window=-1, causal=False)
+    np.testing.assert_allclose(out[0, 0, 0], [math.exp(s12) / z, math.exp(s12) / z, 1 / z], atol=1e-14)
+    assert abs(lse[0, 0, 0] - math.log(z)) < 1e-14
+    assert abs(out[0, 0, 0, 0] - 0.445808) < 1e-6 and abs(out[0, 0, 0, 2] - 0.108384) < 1e-6
+
+
+# ---------------------------------------------------------------------------------------------
+# Brute force with math.fsum on tiny inputs.
+# ---------------------------------------------------------------------------------------------
+
+def brute_attention(q, k, v, window, causal):
+    """Pure-Python attention of one head: q, k [T][d], v [T][dv] as nested lists."""
+    T, d = len(q), len(q[0])
+    dv = len(v[0])
+    out, lse = [], []
+    for i in range(T):
+        keys = [j for j in range(T)
+                if (not causal) or (j <= i and (window < 0 or i - j <= window))]
+        s = {j: math.fsum(q[i][a] * k[j][a] for a in range(d)) / math.sqrt(d) for j in keys}
+        m = max(s.values())
+        l = m + math.log(math.fsum(math.exp(s[j] - m) for j in keys))
+        out.append([math.fsum(math.exp(s[j] - l) * v[j][c] for j in keys) for c in range(dv)])
+        lse.append(l)
+    return out, lse
+
+
+def check_brute_force(o, Ts=(1, 2, 5, 9), ds=(2, 4, 8), seed=0):
+    rng = _rng(seed)
+    for T in Ts:
+        for d in ds:
+            q = rng.standard_normal((1, 2, T, d)) * 1.5
+            k = rng.standard_normal((1, 2, T, d)) * 1.5
+            v = rng.standard_normal((1, 2, T, d + 1))
+            cases = [(-1, False)] + [(w, True) for w in [-1] + list(range(0, T + 2))]
+            for window, causal in cases:
+                out, lse = o.attention(q, k, v, window=window, causal=causal)
+                for h in range(2):
+                    bo, bl = brute_attention(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(),
+                                             window, causal)
+                    np.testing.assert_allclose(out[0, h], np.array(bo), rtol=0, atol=1e-12,
+                                               err_msg=f"T={T} d={d} W={window} causal={causal}")
+                    np.testing.assert_allclose(lse[0, h], np.array(bl), rtol=0, atol=1e-12)
+
+
+def check_sdpa_special_case(o, seed=1):
+    """With no prologue, the oracle equals PyTorch's CPU scaled_dot_product_attention in fp64
+    with an explicit boolean mask built from the window reading."""
+    import torch
+    rng = _rng(seed)
+    B, H, T, d = 2, 3, 37, 16
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, H, T, d))
+    v = rng.standard_normal((B, H, T, d))
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    for window, causal in [(-1, True), (0, True), (5, True), (18, True), (T, True), (-1, False)]:
+        if causal:
+            mask = (j <= i) & ((i - j <= window) if window >= 0 else True)
+        else:
+            mask = np.ones((T, T), dtype=bool)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=torch.from_numpy(np.ascontiguousarray(mask)))
+        out, _ = o.attention(q, k, v, window=window, causal=causal)
+        np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12,
+                                   err_msg=f"W={window} causal={causal}")
+
+
+# ---------------------------------------------------------------------------------------------
+# Invariants of the definition.
+# ---------------------------------------------------------------------------------------------
+
+def check_weights_sum_to_one(o, seed=2):
+    """sum_j exp(s_ij - LSE_i) over the visible keys is 1, with s recomputed by einsum."""
+    rng = _rng(seed)
+    B, H, T, d = 1, 2, 50, 8
+    q = rng.standard_normal((B, H, T, d)) * 2
+    k = rng.standard_normal((B, H, T, d)) * 2
+    v = rng.standard_normal((B, H, T, d))
+    for window in (-1, 0, 7, 25):
+        _, lse = o.attention(q, k, v, window=window, causal=True)
+        s = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(d)
+        i = np.arange(T)[:, None]
+        j = np.arange(T)[None, :]
+        vis = (j <= i) & (((i - j) <= window) if window >= 0 else True)
+        tot = np.where(vis, np.exp(s - lse[..., None]), 0.0).sum(-1)
+        np.testing.assert_allclose(tot, 1.0, rtol=0, atol=1e-13)
+
+
+def check_masked_entries_have_no_weight(o, seed=3):
+    """Rewriting k and v at keys a row cannot see leaves that row bitwise unchanged."""
+    rng = _rng(seed)
+    T, d = 40, 8
+    q = rng.standard_normal((1, 1, T, d))
+    k = rng.standard_normal((1, 1, T, d))
+    v = rng.standard_normal((1, 1, T, d))
+    for window in (-1, 3, 10):
+        out, lse = o.attention(q, k, v, window=window, causal=True)
+        for i in (0, 5, 17, 39):
+            k2, v2 = k.copy(), v.copy()
+            for j in range(T):
+                if j > i or (window >= 0 and i - j > window):
+                    k2[0, 0, j] = 1e4 * (-1) ** j
+                    v2[0, 0, j] = -1e4 * (-1) ** j
+            out2, lse2 = o.attention(q, k2, v2, window=window, causal=True)
+            assert np.array_equal(out2[0, 0, i], out[0, 0, i]), (window, i)
+            assert lse2[0, 0, i] == lse[0, 0, i], (window, i)
+
+
+def check_window_T_is_causal(o, seed=4):
+    """window >= T - 1 (in particular window = T) is the full causal mask."""
+    rng = _rng(seed)
+    T, d = 33, 4
+    q, k, v = (rng.standard_normal((1, 2, T, d)) for _ in range(3))
+    ref = o.attention(q, k, v, window=-1, causal=True)
+    for window in (T - 1, T, 5 * T):
+        out = o.attention(q, k, v, window=window, causal=True)
+        np.testing.assert_allclose(out[0], ref[0], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(out[1], ref[1], rtol=0, atol=1e-15)
+    # window T - 2 is not: the last row loses key 0.
+    out = o.attention(q, k, v, window=T - 2, causal=True)
+    assert not np.allclose(out[0][0, 0, T - 1], ref[0][0, 0, T - 1])
+
+
+def check_window_zero(o, seed=5):
+    """window = 0: each row sees only itself, so O_i = v_i and LSE_i = q_i.k_i / sqrt(d)."""
+    rng = _rng(seed)
+    T, d = 20, 8
+    q, k, v = (rng.standard_normal((1, 1, T, d)) for _ in range(3))
+    out, lse = o.attention(q, k, v, window=0, causal=True)
+    np.testing.assert_allclose(out, v, rtol=0, atol=1e-15)
+    s = np.array([math.fsum(q[0, 0, i] * k[0, 0, i]) / math.sqrt(d) for i in range(T)])
+    np.testing.assert_allclose(lse[0, 0], s, rtol=0, atol=1e-14)
+
+
+def check_zero_query_closed_form(o, seed=6):
+    """Raw q = 0 through the whole layer: QK-norm maps 0 to 0 (eps > 0), every score is 0, so
+    O_i is the mean of the visible v_j and LSE_i = ln |A(i)| = ln(min(i, W) + 1) (inclusive window
+    reading). The exclusive reading (i - j < W) would give ln(min(i + 1, W))."""
+    rng = _rng(seed)
+    T, d = 24, 8
+    q = np.zeros((1, 1, T, d))
+    k = rng.standard_normal((1, 1, T, d))
+    v = rng.standard_normal((1, 1, T, d))
+    for window in (-1, 0, 1, 5, 23):
+        out, lse = o.attention_layer(q, k, v, window=window, causal=True)
+        for i in range(T):
+            n = (i + 1) if window < 0 else (min(i, window) + 1)
+            lo = i + 1 - n
+            np.testing.assert_allclose(out[0, 0, i], v[0, 0, lo:i + 1].mean(0), rtol=0, atol=1e-14)
+            assert abs(lse[0, 0, i] - math.log(n)) < 1e-14, (window, i)
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm and RoPE.
+# ---------------------------------------------------------------------------------------------
+
+def check_rms_norm(o, seed=7):
+    """Mean square of the output is m / (m + eps), where m is the input's mean square; scaling x
+    by c and eps by c^2 leaves the output unchanged; equals torch's CPU rms_norm in fp64."""
+    import torch
+    rng = _rng(seed)
+    x = rng.standard_normal((5, 7, 64)) * rng.uniform(0.01, 10, size=(5, 7, 1))
+    eps = 1e-6
+    y = o.rms_norm(x, eps)
+    m = (x ** 2).mean(-1)
+    np.testing.assert_allclose((y ** 2).mean(-1), m / (m + eps), rtol=1e-14)
+    np.testing.assert_allclose(o.rms_norm(3.0 * x, 9 * eps), y, rtol=1e-14)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), eps=eps).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-15)
+    # a zero row stays zero
+    assert np.all(o.rms_norm(np.zeros((2, 8)), eps) == 0)
+
+
+def check_rope_special_values(o):
+    """Position 0 is the identity. Rotating the unit vector e_0 at position 1 turns the plane
+    (0, d/2) by exactly 1 rad (frequency base**0 = 1): it becomes cos(1) e_0 - sin(1) e_{d/2}.
+    Channel pair d/4 has frequency base**(-1/2) = 1/100, so at position 100 it also turns by 1 rad.
+    """
+    d, T = 16, 101
+    h = d // 2
+    cos, sin = o.rope_cos_sin(T, d, 10000.0)
+    x = np.zeros((T, d))
+    x[:, 0] = 1.0
+    x[:, h // 2] = 2.0
+    y = o.rope_apply(x, cos, sin)
+    np.testing.assert_allclose(y[0], x[0], rtol=0, atol=0)
+    e = np.zeros(d)
+    e[0] = 0.5403023058681398   # cos(1)
+    e[h] = -0.8414709848078965  # -sin(1)
+    e[h // 2] = 2.0 * math.cos(0.01)
+    e[h + h // 2] = -2.0 * math.sin(0.01)
+    np.testing.assert_allclose(y[1], e, rtol=0, atol=1e-15)
+    # position 100, pair d/4: angle 100 * 10000**(-1/2) = 1 rad
+    assert abs(y[100, h // 2] - 2.0 * 0.5403023058681398) < 1e-13
+    assert abs(y[100, h + h // 2] + 2.0 * 0.8414709848078965) < 1e-13
+
+
+def check_rope_invariants(o, seed=8):
+    """The rotation keeps every row's norm, only mixes channel j with j + d/2, and the dot
+    product of a rotated query and key depends only on their distance."""
+    rng = _rng(seed)
+    T, d = 40, 32
+    cos, sin = o.rope_cos_sin(T, d, 10000.0)
+    x = rng.standard_normal((3, T, d))
+    y = o.rope_apply(x, cos, sin)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    # pairing: a unit vector on channel j stays inside the plane (j, j + d/2)
+    for j in (0, 3, d // 2 - 1):
+        e = np.zeros((T, d))
+        e[:, j] = 1.0
+        ye = o.rope_apply(e, cos, sin)
+        others = np.delete(ye, [j, j + d // 2], axis=-1)
+        assert np.all(others == 0)
+    # relative position: same q vector at every position and same k vector at every position
+    qv = rng.standard_normal(d)
+    kv = rng.standard_normal(d)
+    qr = o.rope_apply(np.tile(qv, (T, 1)), cos, sin)
+    kr = o.rope_apply(np.tile(kv, (T, 1)), cos, sin)
+    dots = qr @ kr.T
+    for delta in (0, 1, 7, 20):
+        diag = np.array([dots[i, i - delta] for i in range(delta, T)])
+        np.testing.assert_allclose(diag, diag[0], rtol=0, atol=1e-12)
+
+
+def check_norm_rope_commute(o, seed=9):
+    """QK-norm and RoPE commute (the rotation keeps the sum of squares): both orders agree."""
+    rng = _rng(seed)
+    T, d = 30, 64
+    x = rng.standard_normal((2, 3, T, d)) * 3
+    cos, sin = o.rope_cos_sin(T, d, 10000.0)
+    a = o.rope_apply(o.rms_norm(x, 1e-6), cos, sin)
+    b = o.rms_norm(o.rope_apply(x, cos, sin), 1e-6)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    qn, kn = o.qknorm_rope(x, 2 * x, 1e-6, 10000.0)
+    np.testing.assert_allclose(qn, a, rtol=0, atol=1e-15)
+
+
+def check_sssl_windows(o):
+    """The SSSL schedule: pattern letter per layer, S = T // 2, L = T, last layer forced to L."""
+    assert o.sssl_windows(1024, 4) == [512, 512, 512, 1024]
+    assert o.sssl_windows(8192, 4) == [4096, 4096, 4096, 8192]
+    assert o.sssl_windows(2048, 8) == [1024, 1024, 1024, 2048, 1024, 1024, 1024, 2048]
+    assert o.sssl_windows(1024, 6) == [512, 512, 512, 1024, 512, 1024]
+    assert o.sssl_windows(1024, 2, "S") == [512, 1024]
+    assert o.sssl_windows(1024, 1) == [1024]
+    assert o.sssl_windows(1025, 3, "ss") == [512, 512, 1025]
+
+
+ALL_CHECKS = [
+    check_worked_example,
+    check_worked_example_qknorm,
+    check_brute_force,
+    check_sdpa_special_case,
+    check_weights_sum_to_one,
+    check_masked_entries_have_no_weight,
+    check_window_T_is_causal,
+    check_window_zero,
+    check_zero_query_closed_form,
+    check_rms_norm,
+    check_rope_special_values,
+    check_rope_invariants,
+    check_norm_rope_commute,
+    check_sssl_windows,
+]
