@@ -1,0 +1,128 @@
+/*
+ * attn.h — C ABI of libattn.so: QK-RMSNorm + RoPE + causal / sliding-window attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (page title, then the part of the page):
+ *   [HABR] "Подробный технический разбор реализации Autoresearch, ИИ-исследователя Андрея
+ *          Карпаты" (habr.com, article 1010198), its train.py listing: `norm`,
+ *          `apply_rotary_emb`, `GPT._precompute_rotary_embeddings`,
+ *          `GPT._compute_window_sizes`, `CausalSelfAttention.forward`.
+ *   [GEOM] "Projeção em um Subespaço de Consulta" (unhomeschool.com, geometry_of_andrea),
+ *          sections "O que a Atenção Calcula", "A Máscara Causal", "Escalonamento por sqrt(d_k)".
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, contiguous, row-major [B][H][T][d] (batch, head, token, channel).
+ *   - Pointers named as device pointers must point to device memory of the current HIP device;
+ *     the caller allocates and frees all of them. The library allocates no memory, keeps no
+ *     mutable global state, never synchronises the host, and is safe to call from several
+ *     threads (the calls are ordered only by the stream the caller passes).
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream. Work is only
+ *     enqueued: results are ready once that stream has been synchronised.
+ *   - Every entry point validates its arguments before making any HIP call and returns one of the
+ *     ATTN_* codes below; on an error no work is enqueued. A kernel fault is not reported by the
+ *     call that launched it but by the caller's next synchronisation of the stream.
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out (the prologue and attention compute in fp32 internally). */
+typedef enum attn_dtype {
+  ATTN_BF16 = 0, /* bfloat16; matrix products on bf16 MFMA with fp32 accumulation */
+  ATTN_F32 = 1   /* float32; all arithmetic in fp32 */
+} attn_dtype;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* B, H or T < 1, or an element count that overflows int64 */
+  ATTN_ERR_HEAD_DIM = 3,    /* head dim d not supported for this entry point and dtype */
+  ATTN_ERR_DTYPE = 4,       /* dtype is not an attn_dtype value */
+  ATTN_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_WINDOW = 6,      /* causal is not 0/1, or causal == 0 with window >= 0 */
+  ATTN_ERR_ALIAS = 7,       /* out or lse overlaps an input it must not overlap */
+  ATTN_ERR_ARG = 8,         /* another argument is out of range (eps, base, pattern, n_layer) */
+  ATTN_ERR_HIP = 9          /* the HIP runtime refused the launch */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_strerror(int code);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int attn_version(void);
+
+/*
+ * Per-layer attention windows of a layer pattern such as "SSSL" ([HABR]
+ * `GPT._compute_window_sizes`): layer l uses pattern[l % len(pattern)]; 'L' is T (full causal)
+ * and 'S' is T / 2 (integer division); the last layer is always 'L'. Letters are
+ * case-insensitive.
+ *   T          sequence length, >= 1
+ *   n_layer    number of layers, >= 1
+ *   pattern    NUL-terminated, non-empty, only 'S'/'L' (either case)
+ *   windows    HOST pointer to n_layer ints, written on success
+ * Host-only: makes no HIP call.
+ */
+int attn_sssl_windows(int T, int n_layer, const char* pattern, int* windows);
+
+/*
+ * RoPE tables ([HABR] `GPT._precompute_rotary_embeddings`): for t < T and j < d/2,
+ * theta = t * base^(-2j/d), cos_tab[t][j] = cos(theta), sin_tab[t][j] = sin(theta).
+ * The angles and their cosines and sines are computed in fp64 on the device and rounded to fp32.
+ *   cos_tab, sin_tab   DEVICE pointers to fp32 [T][d/2], written
+ *   T >= 1; d even with 2 <= d <= 256; base > 1
+ */
+int attn_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base, void* stream);
+
+/*
+ * QK-norm then RoPE on q and k ([HABR] `norm`, `apply_rotary_emb` and their use in
+ * `CausalSelfAttention.forward`). For every row x (one token of one head) of q and of k:
+ *   r = 1 / sqrt(mean_j x_j^2 + eps), x <- r * x                       (weightless RMSNorm)
+ *   with h = d/2 and position t (the row's token index):
+ *   y_j     =  x_j * cos[t][j] + x_{j+h} * sin[t][j]
+ *   y_{j+h} = -x_j * sin[t][j] + x_{j+h} * cos[t][j]                   (half-split rotation)
+ * The rotation preserves the row's sum of squares, so normalising before or after it gives the
+ * same result. Arithmetic is fp32; bf16 outputs are rounded to nearest even.
+ *   q, k            DEVICE [B][H][T][d] of dtype, read
+ *   q_out, k_out    DEVICE [B][H][T][d] of dtype, written; q_out may equal q and k_out may equal
+ *                   k (in place); any other overlap is ATTN_ERR_ALIAS
+ *   cos_tab, sin_tab DEVICE fp32 [T][d/2] from attn_rope_table (only rows t < T are read)
+ *   d in {16, 32, 64, 128}; eps >= 0 and finite
+ */
+int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
+                     const float* cos_tab, const float* sin_tab,
+                     int B, int H, int T, int d, float eps, int dtype, void* stream);
+
+/*
+ * Attention forward ([GEOM] "O que a Atenção Calcula", "Escalonamento por sqrt(d_k)",
+ * "A Máscara Causal"; window as in [HABR] `CausalSelfAttention.forward`, which calls the
+ * attention kernel with window_size = (W, 0)):
+ *   s_ij   = q_i . k_j / sqrt(d)
+ *   A(i)   = { j : j <= i and (window < 0 or i - j <= window) }   if causal == 1
+ *            { all j < T }                                        if causal == 0
+ *   lse_i  = ln sum_{j in A(i)} exp(s_ij)                         (natural log, fp32)
+ *   out_i  = sum_{j in A(i)} exp(s_ij - lse_i) v_j
+ * A(i) is never empty. window >= T - 1 is the same as window = -1 (full causal).
+ *   q, k, v   DEVICE [B][H][T][d] of dtype, read
+ *   out       DEVICE [B][H][T][d] of dtype, written; must not overlap q, k, v or lse
+ *   lse       DEVICE fp32 [B][H][T], written; may be NULL (then not written)
+ *   window    -1 = unlimited, >= 0 = causal band width (keys i-window .. i)
+ *   causal    1 = causal mask, 0 = every key visible (requires window == -1)
+ *   d         dtype ATTN_BF16: {32, 64, 128}; ATTN_F32: {16, 32, 64, 128}
+ * bf16: q k^T and P v run on bf16 MFMA with fp32 accumulation; the softmax is fp32 and the
+ * probabilities are rounded to bf16 (nearest even) before the P v product; out is rounded to
+ * nearest even. f32: every step in fp32.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int T, int d, int window, int causal, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */
