@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of the attention block (QK-RMSNorm + RoPE + causal / sliding-window attention
+forward) on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input: for each layer of the
+ANDREA-120M SSSL stack (B=16, H=12, T=1024, d=64, bf16; windows 512, 512, 512, 1024), the fused
+QK-RMSNorm + RoPE prologue on that layer's q and k, then the attention forward with that
+layer's window. Inputs are resident in HBM before timing starts; every layer has its own
+buffers.
+
+The value is counted the way the metric names it: TFLOP/s of unmasked attention work
+(4 d FLOPs per visible (query, key) pair) over the whole step's time, prologue included.
+It prints ONE JSON line on stdout.
+
+Extra modes (used to collect rocprofv3 counters; they print no JSON):
+  --only attn|prologue   run only that kernel, --steps times, after the inputs are ready
+  --copy-calibration     run a plain 256 MiB device copy (known bytes) for counter scaling
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+METRIC = "bf16 causal/SWA attention fwd TFLOP/s + % MFMA peak, T=1024 H=12 d=64"
+ATTN_SOURCE = os.path.join(ROOT, "transformer_attention_qk_amd", "csrc", "attn_fwd_bf16.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_andrea120m_sssl_traffic.md")
+
+
+def visible_pairs(T: int, window: int, causal: bool = True) -> int:
+    """Number of (query, key) pairs the mask keeps in one head (closed form)."""
+    if not causal:
+        return T * T
+    if window < 0 or window >= T - 1:
+        return T * (T + 1) // 2
+    W = window
+    return W * (W + 1) // 2 + (T - W) * (W + 1)
+
+
+def attn_flops(B: int, H: int, T: int, d: int, window: int) -> int:
+    """Unmasked attention FLOPs of one layer: 2 d for q.k plus 2 d for p v per visible pair."""
+    return 4 * d * visible_pairs(T, window) * B * H
+
+
+def attn_compulsory_bytes(B: int, H: int, T: int, d: int, elem: int = 2) -> int:
+    """HBM bytes one attention launch must move: q, k, v read, out written, fp32 lse written."""
+    return B * H * T * (4 * d * elem + 4)
+
+
+def prologue_bytes(B: int, H: int, T: int, d: int, elem: int = 2) -> int:
+    """HBM bytes of one prologue launch: q, k read and written (the RoPE table is cached)."""
+    return B * H * T * 4 * d * elem
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic() -> float | None:
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != source_sha(ATTN_SOURCE):
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(index: int, windows: list[int], budget_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of the same workload: whole heads, all layers, in
+    (b, h) order, until the time budget is spent. Returns TFLOP/s on the same unmasked-FLOP
+    numerator as the GPU."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from transformer_attention_qk_amd import inputs
+
+    w = inputs.WORKLOADS[index]
+    layer_inputs = [inputs.make_qkv(index, l) for l in range(len(windows))]
+    flops = 0
+    heads = 0
+    elapsed = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            per_layer = [tuple(x[b:b + 1, h:h + 1].to(torch.float64).numpy() for x in li)
+                         for li in layer_inputs]
+            t0 = time.perf_counter()
+            for (q, k, v), W in zip(per_layer, windows):
+                oracle.attention_layer(q, k, v, window=W)
+            elapsed += time.perf_counter() - t0
+            flops += sum(attn_flops(1, 1, w.T, w.d, W) for W in windows)
+            heads += 1
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    del np
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{heads} of {w.B * w.H} heads (b, h order), all {len(windows)} layers of "
+                   f"{w.name}: fp64 QK-norm + RoPE + attention, {elapsed:.1f} s; "
+                   f"cores = BLAS threads; host has {len(os.sched_getaffinity(0))} cores"),
+        "seconds": elapsed,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="andrea120m_sssl")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--only", choices=["attn", "prologue"], default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the attention path runs on a single MI355X and this "
+              "build has no multi-GPU mode (the sharding plan is described in DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from transformer_attention_qk_amd import _lib, inputs, ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    _lib.load()
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {max(1, args.steps)} copies of {n} bytes read + {n} bytes written",
+              file=sys.stderr)
+        return 0
+
+    index = [w.name for w in inputs.WORKLOADS].index(args.workload)
+    w = inputs.WORKLOADS[index]
+    if w.dtype != "bf16":
+        print("the bench times bf16 workloads", file=sys.stderr)
+        return 2
+    windows = ops.sssl_windows(w.T, w.n_layer, w.pattern)
+    L = len(windows)
+
+    # Inputs resident in HBM, one set of buffers per layer.
+    q, k, v, qn, kn, out, lse = ([] for _ in range(7))
+    for l in range(L):
+        ql, kl, vl = inputs.make_qkv(index, l)
+        q.append(ql.cuda())
+        k.append(kl.cuda())
+        v.append(vl.cuda())
+        qn.append(torch.empty_like(q[-1]))
+        kn.append(torch.empty_like(k[-1]))
+        out.append(torch.empty_like(q[-1]))
+        lse.append(torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda"))
+    cos, sin = ops.rope_table(w.T, w.d)
+    eps = 1e-6
+    torch.cuda.synchronize()
+
+    def prologue(l):
+        ops.qknorm_rope(q[l], k[l], cos, sin, eps, q_out=qn[l], k_out=kn[l])
+
+    def attention(l):
+        ops.attn_fwd(qn[l], kn[l], v[l], window=windows[l], out=out[l], lse=lse[l])
+
+    def step():
+        for l in range(L):
+            prologue(l)
+            attention(l)
+
+    if args.only:
+        for l in range(L):
+            prologue(l)
+        torch.cuda.synchronize()
+        fn = attention if args.only == "attn" else prologue
+        for _ in range(args.steps):
+            for l in range(L):
+                fn(l)
+        torch.cuda.synchronize()
+        print(f"ran {args.only} x {args.steps * L}", file=sys.stderr)
+        return 0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region 1: whole steps, nothing between the kernels.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # Timed region 2: the same steps with HIP events around every launch (the kernels run on
+    # torch's current stream, which is where the events are recorded).
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(L)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for l in range(L):
+            a, b, c = ev[s][l]
+            a.record()
+            prologue(l)
+            b.record()
+            attention(l)
+            c.record()
+    torch.cuda.synchronize()
+    attn_ms = [0.0] * L
+    pro_ms = [0.0] * L
+    for s in range(args.steps):
+        for l in range(L):
+            a, b, c = ev[s][l]
+            pro_ms[l] += a.elapsed_time(b) / args.steps
+            attn_ms[l] += b.elapsed_time(c) / args.steps
+
+    flops_layer = [attn_flops(w.B, w.H, w.T, w.d, W) for W in windows]
+    step_flops = sum(flops_layer)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    attn_total_ms = sum(attn_ms)
+    achieved = step_flops / (attn_total_ms * 1e-3) / 1e12
+    attn_bytes = attn_compulsory_bytes(w.B, w.H, w.T, w.d)
+    pro_bytes = prologue_bytes(w.B, w.H, w.T, w.d)
+    traffic = measured_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "layers": L,
+            "windows": windows, "step": "per layer: qknorm_rope + attn_fwd",
+            "flops_per_step": step_flops,
+        },
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_kernel<64>",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "avg_launch_us": round(1e3 * attn_total_ms / L, 3),
+            "launch_us": [round(1e3 * t, 3) for t in attn_ms],
+            "flops_per_launch": flops_layer,
+            "compulsory_bytes_per_launch": attn_bytes,
+            "compulsory_hbm_gbs": round(attn_bytes * L / (attn_total_ms * 1e-3) / 1e9, 1),
+        },
+        "prologue": {
+            "avg_launch_us": round(1e3 * sum(pro_ms) / L, 3),
+            "bytes_per_launch": pro_bytes,
+            "achieved_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
+            "peak_gbs": PEAK_HBM_GBS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(index, windows, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

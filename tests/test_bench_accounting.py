@@ -1,0 +1,33 @@
+"""The bench's work accounting on the CPU: the closed-form pair count equals the number of
+entries the oracle's mask keeps, and the headline stack comes to 83.89 GFLOP."""
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 17, 64, 130])
+def test_visible_pairs_match_the_oracle_mask(T):
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    for window in [-1, 0, 1, 2, T // 2, T - 2, T - 1, T, 3 * T]:
+        if window < -1:
+            continue
+        n = int(oracle.visible(i, j, window, True).sum())
+        assert bench.visible_pairs(T, window) == n, (T, window)
+    assert bench.visible_pairs(T, -1, causal=False) == int(oracle.visible(i, j, -1, False).sum())
+
+
+def test_headline_stack_flops():
+    wins = oracle.sssl_windows(1024, 4)
+    total = sum(bench.attn_flops(16, 12, 1024, 64, W) for W in wins)
+    assert total == 83_890_274_304  # 3 x 393,984 + 524,800 pairs per head, x 4d x 192 heads
+    assert bench.attn_compulsory_bytes(16, 12, 1024, 64) == 16 * 12 * 1024 * (8 * 64 + 4)
+
+
+def test_bench_refuses_more_than_one_gpu(capsys, monkeypatch):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    assert "one GPU" in capsys.readouterr().err

@@ -134,6 +134,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
         overlap(lse, lbytes, v, bytes) || overlap(lse, lbytes, out, bytes))
       return ATTN_ERR_ALIAS;
   }
+  // One head's [T][d] slab (plus a query block of padding rows) must stay below 2^31 bytes: the
+  // bf16 kernel addresses it through 32-bit buffer offsets.
+  if (dtype == ATTN_BF16 && ((int64_t)T + 128) * d * 2 >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
   const int64_t tiles = (dtype == ATTN_BF16) ? (T + 127) / 128 : (T + 63) / 64;
   if (bh * tiles > kMaxGrid) return ATTN_ERR_SHAPE;
   hipError_t e;

@@ -28,6 +28,14 @@
 //   - Tiles the mask hides completely are never loaded; 32-key blocks a wave cannot see are
 //     skipped by that wave; the elementwise mask is applied only on blocks that straddle the
 //     diagonal, the window edge or the end of the sequence.
+//   - Global loads are buffer loads whose range is the head's [T][d] slab: rows past T read as
+//     zero without a branch, and the prefetch of the tile after the last one is sent out of
+//     range, so every load and LDS store is unconditional and the compiler never has to wait
+//     on a prefetch before it is consumed.
+//   - The running maximum is raised lazily: only when a tile's maximum exceeds it by more than
+//     kRescaleSlack (base-2 units) are the accumulators rescaled. Until then the weights
+//     exp2(s - m) stay below 2^kRescaleSlack, which fp32 sums and bf16 weights hold exactly as
+//     well as weights below 1.
 #include <math.h>
 
 #include "common.hpp"
@@ -67,6 +75,35 @@ __device__ __forceinline__ int swz_v(int r) {
 
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 
+constexpr float kRescaleSlack = 8.0f;
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs: 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+// Offset past any head slab (slabs are < 2^31 bytes): such buffer loads return zero.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Lanes l and l + 32 hold the same query row. v_permlane32_swap exchanges the upper half of one
+// register with the lower half of another; applied to two copies of x, each lane ends up holding
+// its own value in one result and its partner's in the other, so the max (or sum) of the two
+// results is the pair's max (or sum) in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+}
+
 __device__ __forceinline__ u32x2 ds_read_tr16_b64(const char* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_i16x4_ptr)((__attribute__((address_space(3))) char*)(p)));
@@ -82,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -94,16 +131,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int qw0 = q0 + 32 * wave;
   const int qi = qw0 + l32;  // the query this lane owns in S^T and O^T
 
-  // Q^T fragments (B operand): lane holds Q[qi][16 s + 8 hi .. +8).
+  const int slab = T * C::ROW_BYTES;  // bytes of one head's [T][d] slab (< 2^31, checked)
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + hoff, slab);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + hoff, slab);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + hoff, slab);
+
+  // Q^T fragments (B operand): lane holds Q[qi][16 s + 8 hi .. +8); rows past T read as zero.
   bf16x8 qf[C::KSTEPS];
 #pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s) {
-    if (qi < T) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(Q + hoff + (int64_t)qi * D + 16 * s + 8 * hi);
-    } else {
-      qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
-  }
+  for (int s = 0; s < C::KSTEPS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qi * C::ROW_BYTES + 32 * s + 16 * hi)));
 
   // Keys any query of this workgroup can see, and those of this wave.
   int kv_lo = 0, kv_hi = T, w_lo = 0, w_hi = T;
@@ -126,22 +163,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY;  // running maximum of the scaled scores, base-2 units
   float l_run = 0.f;        // this lane's part of the running sum (its 16 keys per block)
 
-  // Global -> register staging of one K and one V tile.
+  // Global -> register staging of one K and one V tile (rows past T read as zero; a tile that
+  // is not needed is sent out of range and costs no memory traffic).
   u32x4 kst[C::LPT], vst[C::LPT];
-  auto gload = [&](int t) {
+  auto gload = [&](int t, bool needed) {
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
       const int e = tid + 256 * u;
-      const int row = t * C::BN + e / C::CH;
-      const int c = e % C::CH;
-      if (row < T) {
-        const int64_t off = hoff + (int64_t)row * D + 8 * c;
-        kst[u] = *reinterpret_cast<const u32x4*>(K + off);
-        vst[u] = *reinterpret_cast<const u32x4*>(V + off);
-      } else {
-        kst[u] = u32x4{0u, 0u, 0u, 0u};
-        vst[u] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const uint32_t off = needed ? (uint32_t)((t * C::BN + e / C::CH) * C::ROW_BYTES + 16 * (e % C::CH))
+                                  : kOutOfRange;
+      kst[u] = buffer_load16(rk, off);
+      vst[u] = buffer_load16(rv, off);
     }
   };
   auto lstore = [&](int buf) {
@@ -168,15 +200,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int v_g1 = (lane >> 4) & 1;
   const int v_swz = swz_v<D>(v_a);  // row = (multiple of 4) + v_a, so the swizzle is lane-constant
 
-  if (t_begin < t_end) {
-    gload(t_begin);
-    lstore(0);
-  }
+  gload(t_begin, true);
+  lstore(0);
   __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) gload(t + 1);
+    gload(t + 1, t + 1 < t_end);
     const char* kbuf = smem + buf * C::STAGE_BYTES;
     const char* vbuf = kbuf + C::TILE_BYTES;
     const int kt0 = t * C::BN;
@@ -195,9 +225,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        if (!active[kb]) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-        if (!active[kb]) continue;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
@@ -228,16 +258,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
+      mx = pair_max(mx);
+      const float m_tile = mx * scale_log2;
+      // Raise the running maximum only when the tile exceeds it by more than the slack (always
+      // on a row's first visible tile, since m_run starts at -inf).
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
       // P = exp2(s * scale - m), rounded to bf16 in the B-operand order of the P V product.
       bf16x8 pf[2][2];
@@ -280,12 +315,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       }
     }
 
-    if (t + 1 < t_end) lstore(buf ^ 1);
+    lstore(buf ^ 1);
     __syncthreads();
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (qi < T) {
     const float inv = 1.0f / l_tot;
     bf16* orow = O + hoff + (int64_t)qi * D;
