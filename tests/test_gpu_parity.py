@@ -22,6 +22,10 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
+# LSE on the bf16 path: the row sums add the bf16-rounded weights (the values the P V product
+# uses), each within a relative 2^-9 of the exact weight, so ln of the sum moves by at most 2^-9;
+# 2^-8 leaves room for the fp32 arithmetic around it.
+BF16_LSE_TOL = 2.0 ** -8
 
 
 def say(*a):
@@ -132,7 +136,7 @@ def test_attn_fwd_raw_parity(dt, d, T, window, causal):
     say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     tol = BF16_TOL if dt == "bf16" else F32_TOL
     assert eo <= tol
-    assert el <= (1e-3 if dt == "bf16" else F32_TOL)
+    assert el <= (BF16_LSE_TOL if dt == "bf16" else F32_TOL)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
@@ -153,7 +157,7 @@ def test_attn_fwd_peaky_scores(d):
         eo = np.max(np.abs(f64(out) - ro))
         say(f"   W={window} max|dO|={eo:.3e} max|dLSE|={np.max(np.abs(f64(lse) - rl)):.3e}")
         assert eo <= BF16_TOL
-        assert np.max(np.abs(f64(lse) - rl)) <= 1e-3 * max(1.0, np.max(np.abs(rl)))
+        assert np.max(np.abs(f64(lse) - rl)) <= BF16_LSE_TOL * max(1.0, np.max(np.abs(rl)))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -264,7 +268,9 @@ def test_worked_example_on_gpu(dt, d, qscale):
     tol = 4e-3 if dt == "bf16" else 1e-6
     assert np.max(np.abs(o[0, :3] - w)) <= tol
     assert np.all(o[0, 3:] == 0)
-    assert abs(float(lse[0, 0, 0]) - math.log(2 * se + 1)) <= 1e-5
+    # bf16: the row sum adds the bf16-rounded weights (e^-0.5 rounds to 0.60546875)
+    ltol = BF16_LSE_TOL if dt == "bf16" else 1e-5
+    assert abs(float(lse[0, 0, 0]) - math.log(2 * se + 1)) <= ltol
     assert np.max(np.abs(o[1:, :3] - 1 / 3)) <= tol
     assert np.max(np.abs(f64(lse)[0, 0, 1:] - math.log(3))) <= 1e-5
 

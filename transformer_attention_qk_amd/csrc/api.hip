@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "launch.hpp"
 
 namespace {
