@@ -10,19 +10,12 @@
 // the tiling and the one-pass (running maximum) softmax below are this library's design.
 //
 // Layout of the work:
-//   - Work items are (batch*head, block of BM = 128 queries). A workgroup of 4 waves owns one
-//     item at a time; wave w owns queries [32w, 32w + 32) of the block.
-//   - The grid is persistent: as many workgroups as the GPU holds at once, each walking its own
-//     list of items. Items are ranked heaviest first (the last query blocks of a causal head see
-//     the most keys) and dealt out in a snake order (rank k*P + g on even passes, k*P + P-1-g on
-//     odd ones), which pairs heavy with light items per workgroup.
-//   - Key/value tiles of BN = 64 rows flow HBM -> registers -> LDS through a 2-slot LDS ring,
-//     one tile ahead, with one barrier per tile. The prefetch runs straight across item
-//     boundaries: while the last tile of an item is consumed, the first tile of the workgroup's
-//     next item is already in flight, so a workgroup never waits on a cold start after its first
-//     item. The next item's Q block is fetched during the current item's first tile into the
-//     other half of a double-buffered LDS Q area (d <= 64; at d = 128 the items are long and Q
-//     is read straight from global memory at item start).
+//   - A workgroup of 4 waves owns BM = 128 consecutive queries of one (batch, head); wave w owns
+//     queries [32w, 32w + 32) of that block. Workgroups are launched heaviest query block first
+//     (the last blocks of a causal head see the most keys).
+//   - Key/value tiles of BN = 64 rows flow HBM -> registers -> LDS through 2-slot LDS rings with
+//     one barrier per tile: V one tile ahead, K two tiles ahead when the loop is pipelined
+//     (below), else one.
 //   - S^T = K Q^T per 32-key block with v_mfma_f32_32x32x16_bf16: A = K from LDS (16 bytes per
 //     lane), B = Q^T kept in registers for the whole workgroup. In the accumulator each lane owns
 //     one query (lane % 32) and 16 keys, so row maxima and sums are lane-local plus one exchange
@@ -31,6 +24,10 @@
 //     bf16), A = V^T read from the row-major V tile with ds_read_b64_tr_b16, which transposes
 //     4x16 blocks of 16-bit values between lanes. The key order inside each 16-key MFMA step
 //     follows the S^T accumulator's register order on both operands.
+//   - Software pipeline inside each wave (d <= 64): the iteration for tile t issues the scores
+//     of tile t+1 on the matrix cores while the vector ALUs exponentiate tile t, then issues
+//     P(t) V(t) while the vector ALUs mask and reduce the scores of tile t+1. Unmasked tiles
+//     (the bulk) run this as one straight-line block with an explicit MFMA / VALU interleave.
 //   - Row sums of the weights are taken with v_dot2_f32_bf16 on the bf16-rounded weights, i.e.
 //     on exactly the values the P V product uses.
 //   - LDS rows are XOR-swizzled in 16-byte chunks so that the K reads (16 rows x 16 bytes per
@@ -57,7 +54,7 @@ namespace attn {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;             // queries per work item
+  static constexpr int BM = 128;             // queries per workgroup
   static constexpr int BN = 64;              // keys per tile
   static constexpr int KSTEPS = D / 16;      // MFMA k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;          // 32-row blocks of O^T
@@ -65,13 +62,18 @@ struct FwdCfg {
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;
   static constexpr int LPT = BN * CH / 256;  // 16-byte chunks per thread per K or V tile
-  static constexpr bool QLDS = D <= 64;      // next item's Q staged through LDS
-  static constexpr int Q_BYTES = BM * ROW_BYTES;
-  static constexpr int QPT = BM * CH / 256;  // 16-byte chunks per thread per Q block
-  // K ring (2 tiles), V ring (2 tiles), then the Q double buffer.
-  static constexpr int KV_BYTES = 4 * TILE_BYTES;
-  static constexpr int LDS_BYTES = KV_BYTES + (QLDS ? 2 * Q_BYTES : 0);
-  static_assert(LPT >= 1 && QPT >= 1, "tile too small for 256 threads");
+  // Software-pipelined loop (two score accumulators live at once) fed by direct global -> LDS
+  // loads for d <= 64; at d = 128 that does not fit the registers of two waves per SIMD, and the
+  // matrix work per tile (twice that of d = 64 for the same softmax work) leaves the vector ALUs
+  // less to hide anyway.
+  static constexpr bool PIPE = D <= 64;
+  // Pipelined: a ring of NSTAGE (K tile, V tile) stages filled PREFETCH tiles ahead.
+  // Otherwise: K ring (2 tiles), then V ring (2 tiles), staged through registers.
+  static constexpr int NSTAGE = 4;
+  static constexpr int PREFETCH = NSTAGE - 1;
+  static constexpr int LDS_BYTES = PIPE ? NSTAGE * 2 * TILE_BYTES : 4 * TILE_BYTES;
+  static constexpr int DMA_PER_TILE = 2 * LPT;  // direct loads per thread per (K, V) tile pair
+  static_assert(LPT >= 1, "tile too small for 256 threads");
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row r of a K tile: quarter-wave K reads
@@ -106,6 +108,35 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Direct global -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane L's bytes
+// land at LDS address lds_base + 16 L (lds_base is wave-uniform, through M0), its source is the
+// buffer offset voff (out of range reads zero). Written in assembly because the compiler, which
+// cannot tell which LDS bytes such a load writes, drains every outstanding one before each
+// barrier; the kernel waits for them itself with s_waitcnt vmcnt. The instruction returns no
+// registers, so nothing in flight can be overwritten.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Raw buffer resource (stride 0) over [base, base + bytes), as four scalar words.
+__device__ __forceinline__ u32x4 head_rsrc_words(const bf16* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  r[3] = (uint32_t)kBufferWord3;
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // Lanes l and l + 32 hold the same query row. v_permlane32_swap exchanges the upper half of one
 // register with the lower half of another; applied to two copies of x, each lane ends up holding
 // its own value in one result and its partner's in the other, so the max (or sum) of the two
@@ -136,6 +167,11 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
 // Mask of a launch, fixed at compile time so the per-element test is exactly what is needed.
 enum MaskMode { kNonCausal = 0, kCausal = 1, kCausalWindow = 2 };
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt left unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -151,45 +187,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int P = (int)gridDim.x;
-  const int g = (int)blockIdx.x;
-  const int n_items = BH * nqt;
+
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest query block first
+  const int bh = (int)(blockIdx.x % BH);
+  const int64_t hoff = (int64_t)bh * T * D;
+  const int q0 = qt * C::BM;
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + l32;  // the query this lane owns in S^T and O^T
+
   const int slab = T * C::ROW_BYTES;  // bytes of one head's [T][d] slab (< 2^31, checked)
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + hoff, slab);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + hoff, slab);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + hoff, slab);
 
-  // Item list of this workgroup: heaviest-first ranks dealt out in snake order.
-  auto rank_of = [&](int k) { return k * P + ((k & 1) ? (P - 1 - g) : g); };
-  auto decode = [&](int rank, int& bh, int& q0, int& tb, int& te) {
-    const int qt = nqt - 1 - rank / BH;
-    bh = rank % BH;
-    q0 = qt * C::BM;
-    int lo = 0, up = T;
-    if constexpr (causal) {
-      up = min(T, q0 + C::BM);
-      if constexpr (MODE == kCausalWindow) lo = max(0, q0 - window);
+  // Keys any query of the workgroup sees: [kv_lo, kv_hi). Keys some query of this wave sees:
+  // [w_lo, w_hi); keys every query of the wave sees (no mask needed): [f_lo, f_hi).
+  int kv_lo = 0, kv_hi = T, w_lo = 0, w_hi = T, f_lo = 0, f_hi = T;
+  if constexpr (causal) {
+    kv_hi = min(T, q0 + C::BM);
+    w_hi = min(T, qw0 + 32);
+    f_hi = min(T, qw0 + 1);
+    if constexpr (MODE == kCausalWindow) {
+      kv_lo = max(0, q0 - window);
+      w_lo = max(0, qw0 - window);
+      f_lo = qw0 + 31 - window;
     }
-    tb = lo / C::BN;
-    te = (up + C::BN - 1) / C::BN;
-  };
-
-  // Per-item, per-wave key ranges: keys some query of the wave sees are [w_lo, w_hi); keys every
-  // query of the wave sees (no mask needed) are [f_lo, f_hi).
-  int qw0 = 0, qi = 0, w_lo = 0, w_hi = T, f_lo = 0, f_hi = T;
-  auto setup_wave = [&](int q0) {
-    qw0 = q0 + 32 * wave;
-    qi = qw0 + l32;  // the query this lane owns in S^T and O^T
-    w_lo = 0;
-    w_hi = T;
-    f_lo = 0;
-    f_hi = T;
-    if constexpr (causal) {
-      w_hi = min(T, qw0 + 32);
-      f_hi = min(T, qw0 + 1);
-      if constexpr (MODE == kCausalWindow) {
-        w_lo = max(0, qw0 - window);
-        f_lo = qw0 + 31 - window;
-      }
-    }
-  };
+  }
+  const int t_begin = kv_lo / C::BN;
+  const int t_end = (kv_hi + C::BN - 1) / C::BN;
   auto active = [&](int t, int kb) {
     const int b0 = t * C::BN + 32 * kb;
     return (b0 < w_hi) && (b0 + 32 > w_lo);
@@ -198,55 +223,47 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const int b0 = t * C::BN + 32 * kb;
     return (b0 >= f_lo) && (b0 + 32 <= f_hi);
   };
+  auto fast = [&](int t) { return full(t, 0) && full(t, 1); };
 
-  // ---- global -> register staging -------------------------------------------------------
-  u32x4 kst[C::LPT], vst[C::LPT], qst[C::QPT];
-  auto gload_kv = [&](int bh, int t, bool needed) {
-    const int64_t hoff = (int64_t)bh * T * D;
-    const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + hoff, slab);
-    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + hoff, slab);
+  // Q^T fragments (B operand): lane holds Q[qi][16 s + 8 hi .. +8); rows past T read as zero.
+  bf16x8 qf[C::KSTEPS];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qi * C::ROW_BYTES + 32 * s + 16 * hi)));
+  };
+
+  // ---- global -> register staging, LDS stores ---------------------------------------------
+  auto gload = [&](__amdgpu_buffer_rsrc_t r, int t, bool needed, u32x4(&st)[C::LPT]) {
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
       const int e = tid + 256 * u;
       const uint32_t off =
           needed ? (uint32_t)((t * C::BN + e / C::CH) * C::ROW_BYTES + 16 * (e % C::CH)) : kOutOfRange;
-      kst[u] = buffer_load16(rk, off);
-      vst[u] = buffer_load16(rv, off);
+      st[u] = buffer_load16(r, off);
     }
   };
-  auto gload_q = [&](int bh, int q0) {
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + (int64_t)bh * T * D, slab);
-#pragma unroll
-    for (int u = 0; u < C::QPT; ++u) {
-      const int e = tid + 256 * u;
-      qst[u] = buffer_load16(rq, (uint32_t)((q0 + e / C::CH) * C::ROW_BYTES + 16 * (e % C::CH)));
-    }
-  };
-  // ---- LDS stores (16-byte chunks, XOR-swizzled rows) ------------------------------------
-  auto lstore_kv = [&](int slot) {
-    char* kb_ = smem + slot * C::TILE_BYTES;
-    char* vb_ = smem + (2 + slot) * C::TILE_BYTES;
+  auto lstore_k = [&](int slot, const u32x4(&st)[C::LPT]) {
+    char* base = smem + slot * C::TILE_BYTES;
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
       const int e = tid + 256 * u;
       const int r = e / C::CH, c = e % C::CH;
-      *reinterpret_cast<u32x4*>(kb_ + r * C::ROW_BYTES + 16 * (c ^ swz_k<D>(r))) = kst[u];
-      *reinterpret_cast<u32x4*>(vb_ + r * C::ROW_BYTES + 16 * (c ^ swz_v<D>(r))) = vst[u];
+      *reinterpret_cast<u32x4*>(base + r * C::ROW_BYTES + 16 * (c ^ swz_k<D>(r))) = st[u];
     }
   };
-  auto lstore_q = [&](int buf) {
-    char* qb = smem + C::KV_BYTES + buf * C::Q_BYTES;
+  auto lstore_v = [&](int slot, const u32x4(&st)[C::LPT]) {
+    char* base = smem + (2 + slot) * C::TILE_BYTES;
 #pragma unroll
-    for (int u = 0; u < C::QPT; ++u) {
+    for (int u = 0; u < C::LPT; ++u) {
       const int e = tid + 256 * u;
       const int r = e / C::CH, c = e % C::CH;
-      *reinterpret_cast<u32x4*>(qb + r * C::ROW_BYTES + 16 * (c ^ swz_k<D>(r))) = qst[u];
+      *reinterpret_cast<u32x4*>(base + r * C::ROW_BYTES + 16 * (c ^ swz_v<D>(r))) = st[u];
     }
   };
 
   // Lane-constant parts of the LDS read addresses.
-  // K (A operand of S^T): row 32 kb + l32, logical chunk 2 s + hi. The Q block uses the same
-  // layout, wave w reading rows 32 w + l32 (the swizzle of those rows equals that of l32).
+  // K (A operand of S^T): row 32 kb + l32, logical chunk 2 s + hi.
   const int k_row_off = l32 * C::ROW_BYTES;
   const int k_swz = swz_k<D>(l32);
   // V (A operand of O^T via the transposing read): lane (4a + b) of each 16-lane group addresses
@@ -256,77 +273,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int v_g1 = (lane >> 4) & 1;
   const int v_swz = swz_v<D>(v_a);  // row = (multiple of 4) + v_a, so the swizzle is lane-constant
 
-  // Q^T fragments (B operand of S^T): lane holds Q[qi][16 s + 8 hi .. +8).
-  bf16x8 qf[C::KSTEPS];
-  auto q_from_global = [&](int bh) {
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + (int64_t)bh * T * D, slab);
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qi * C::ROW_BYTES + 32 * s + 16 * hi)));
-  };
-  auto q_from_lds = [&](int buf) {
-    const char* qb = smem + C::KV_BYTES + buf * C::Q_BYTES + 32 * wave * C::ROW_BYTES + k_row_off;
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(qb + 16 * ((2 * s + hi) ^ k_swz));
-  };
-
-  // ---- per-item accumulators --------------------------------------------------------------
-  f32x16 oacc[C::DB];
-  float m_run, l_run0, l_run1;  // running max (base-2 units) and this lane's two partial sums
-  auto reset = [&]() {
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-    m_run = -INFINITY;
-    l_run0 = 0.f;
-    l_run1 = 0.f;
-  };
-
-  // ---- one tile: S^T = K Q^T, mask, softmax, O^T += V^T P^T -------------------------------
-  // FAST: both 32-key blocks visible to every query of the wave. The tile is then one
-  // straight-line block with the two score chains interleaved, which lets the compiler hide LDS
-  // and MFMA latencies behind each other. Otherwise each block is skipped or masked as needed.
-  auto compute_tile = [&](int slot, int t, auto fast_tag) {
+  // ---- stages of a tile ---------------------------------------------------------------------
+  // Scores of tile t (K from ring slot `slot`) for the blocks this wave sees.
+  auto scores = [&](int slot, int t, f32x16(&sa)[2], auto fast_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
+    const char* kb_base = smem + slot * C::TILE_BYTES;
     const bool a0 = FAST || active(t, 0), a1 = FAST || active(t, 1);
-    const char* kbuf = smem + slot * C::TILE_BYTES;
-    const char* vbuf = smem + (2 + slot) * C::TILE_BYTES;
-    f32x16 sa[2];
-    if constexpr (FAST) {
-      sa[0] = f32x16{};
-      sa[1] = f32x16{};
+    if (a0) sa[0] = f32x16{};
+    if (a1) sa[1] = f32x16{};
+    auto step = [&](int s, int kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + 32 * kb * C::ROW_BYTES +
+                                                        k_row_off + 16 * ((2 * s + hi) ^ k_swz));
+      sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sa[kb], 0, 0, 0);
+    };
+    if constexpr (C::PIPE) {
+      // the two accumulation chains interleaved
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + 32 * kb * C::ROW_BYTES +
-                                                            k_row_off + 16 * ((2 * s + hi) ^ k_swz));
-          sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sa[kb], 0, 0, 0);
-        }
+        if (a0) step(s, 0);
+        if (a1) step(s, 1);
       }
     } else {
+      // one block after the other keeps fewer K fragments in flight (register budget at d=128)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (!(kb == 0 ? a0 : a1)) continue;
-        bf16x8 a[C::KSTEPS];
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s)
-          a[s] = *reinterpret_cast<const bf16x8*>(kbuf + 32 * kb * C::ROW_BYTES + k_row_off +
-                                                  16 * ((2 * s + hi) ^ k_swz));
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], qf[s], acc, 0, 0, 0);
-        sa[kb] = acc;
+        for (int s = 0; s < C::KSTEPS; ++s) step(s, kb);
       }
     }
+  };
 
-    // Mask, then the tile's row maximum (raw scores; the scale is positive).
-    float mx = -INFINITY;
+  // Mask the scores of tile t and return their row maximum (raw, pair-reduced).
+  auto mask_max = [&](int t, f32x16(&sa)[2], auto fast_tag) -> float {
+    constexpr bool FAST = decltype(fast_tag)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (!FAST) {
-        if (!(kb == 0 ? a0 : a1)) {
+        if (!active(t, kb)) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) sa[kb][r] = -INFINITY;
           continue;
@@ -349,13 +333,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
           }
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sa[kb][r], sa[kb][r + 1]));
     }
-    mx = pair_max(mx);
+    // Tree reduction over the 32 values of the lane, then across the lane pair.
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      m8[i] = fmaxf(fmaxf(sa[i >> 2][4 * (i & 3)], sa[i >> 2][4 * (i & 3) + 1]),
+                    fmaxf(sa[i >> 2][4 * (i & 3) + 2], sa[i >> 2][4 * (i & 3) + 3]));
+    const float m2a = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+    const float m2b = fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7]));
+    return pair_max(fmaxf(m2a, m2b));
+  };
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;           // running maximum of the scaled scores, base-2 units
+  float l_run0 = 0.f, l_run1 = 0.f;  // this lane's part of the running sum (two chains)
+
+  // Lazy running-maximum update with a tile's row maximum (raw scores).
+  auto decide = [&](float mx) {
     const float m_tile = mx * scale_log2;
-    // Raise the running maximum only when the tile exceeds it by more than the slack (always
-    // on a row's first visible tile, since m_run starts at -inf).
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
@@ -367,11 +365,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  };
 
-    // P = exp2(s * scale - m), rounded to bf16 in the B-operand order of the P V product; the
-    // row sums add the rounded values.
-    bf16x8 pf[2][2];
+  // P = exp2(s * scale - m), rounded to bf16 in the B-operand order of the P V product; the row
+  // sums add the rounded values.
+  auto exps = [&](const f32x16(&sa)[2], bf16x8(&pf)[2][2]) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -390,12 +389,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         pf[kb][tt] = __builtin_bit_cast(bf16x8, w);
       }
     }
+  };
 
-    // O^T += V^T P^T.
+  // O^T += V^T P^T for tile t (V from ring slot `slot`).
+  auto pv = [&](int slot, int t, const bf16x8(&pf)[2][2], auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const char* vb = smem + (2 + slot) * C::TILE_BYTES;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (!FAST) {
-        if (!(kb == 0 ? a0 : a1)) continue;
+        if (!active(t, kb)) continue;
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
           for (int u = 0; u < 2; ++u) {
             const int row = 32 * kb + 16 * tt + 8 * u + 4 * hi + v_a;
             const int c = 4 * db + 2 * v_g1 + (v_b >> 1);
-            part[u] = ds_read_tr16_b64(vbuf + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
+            part[u] = ds_read_tr16_b64(vb + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
           }
           const u32x4 a4{part[0][0], part[0][1], part[1][0], part[1][1]};
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
@@ -415,113 +418,162 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       }
     }
   };
-  auto tile = [&](int slot, int t) {
-    // At d = 128 the straight-line form needs more registers than two waves per SIMD have.
-    if (D <= 64 && full(t, 0) && full(t, 1))
-      compute_tile(slot, t, std::true_type{});
-    else if (active(t, 0) || active(t, 1))
-      compute_tile(slot, t, std::false_type{});
-  };
 
-  // ---- epilogue of an item: O = O^T / l, LSE = (m + log2 l) ln 2 -------------------------
-  auto epilogue = [&](int bh) {
-    const float l_tot = pair_sum(l_run0 + l_run1);
-    if (qi < T) {
-      const float inv = 1.0f / l_tot;
-      bf16* orow = O + (int64_t)bh * T * D + (int64_t)qi * D;
+  if constexpr (C::PIPE) {
+    // Stage st holds a K tile then a V tile; tile t lives in stage (t - t0) % NSTAGE.
+    const u32x4 rk_w = head_rsrc_words(K + hoff, slab);
+    const u32x4 rv_w = head_rsrc_words(V + hoff, slab);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+    // Issue the direct loads of tile t (out of range when not needed) into stage st. Wave w
+    // fills 1 KiB runs (w * LPT + u) of each tile; lane L of a run writes chunk p = run * 64 + L,
+    // i.e. row p / CH at physical chunk p % CH, so it loads the logical chunk that the row's
+    // swizzle puts there.
+    auto dma_tile = [&](int t, bool needed, int st) {
+      const uint32_t kb_ = lds0 + st * 2 * C::TILE_BYTES;
+      const uint32_t vb_ = kb_ + C::TILE_BYTES;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[db][4 * gg] * inv, oacc[db][4 * gg + 1] * inv);
-          w[1] = pack_bf16x2(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * gg + 4 * hi) = w;
-        }
+      for (int u = 0; u < C::LPT; ++u) {
+        const int run = wave * C::LPT + u;
+        const int p = run * 64 + lane;
+        const int r = p / C::CH, pc = p % C::CH;
+        const uint32_t row_off = (uint32_t)((t * C::BN + r) * C::ROW_BYTES);
+        dma16(rk_w, kb_ + run * 1024, needed ? row_off + 16 * (pc ^ swz_k<D>(r)) : kOutOfRange);
+        dma16(rv_w, vb_ + run * 1024, needed ? row_off + 16 * (pc ^ swz_v<D>(r)) : kOutOfRange);
       }
-      if (hi == 0 && LSE != nullptr) LSE[(int64_t)bh * T + qi] = (m_run + __log2f(l_tot)) * kLn2;
-    }
-  };
+    };
+    auto kslot = [&](int t) { return 2 * ((t - t_begin) % C::NSTAGE); };      // K ring slot
+    auto vslot = [&](int t) { return 2 * ((t - t_begin) % C::NSTAGE) - 1; };  // V, as pv() adds 2
 
-  // ---- the item stream ---------------------------------------------------------------------
-  int k = 0;
-  int bh, q0, tb, te;
-  decode(rank_of(0), bh, q0, tb, te);  // g < P <= n_items
-  setup_wave(q0);
-  q_from_global(bh);
-  gload_kv(bh, tb, true);
-  lstore_kv(0);
-  reset();
-  __syncthreads();
-
-  // The workgroup's next item, if any.
-  int rank_n = rank_of(1);
-  bool more = rank_n < n_items;
-  int nbh = 0, nq0 = 0, ntb = 0, nte = 0;
-  if (more) decode(rank_n, nbh, nq0, ntb, nte);
-
-  int t = tb, slot = 0;
-  while (true) {
-    const bool last = (t + 1 == te);
-    // Prefetch the next tile of the stream (it may belong to the next item).
-    if (!last)
-      gload_kv(bh, t + 1, true);
-    else
-      gload_kv(nbh, ntb, more);
-    // During an item's first tile, fetch the next item's Q block.
-    const bool qpref = C::QLDS && more && (t == tb);
-    if (qpref) gload_q(nbh, nq0);
-
-    tile(slot, t);
-    if (last) epilogue(bh);
-
-    lstore_kv(slot ^ 1);
-    if (qpref) lstore_q((k + 1) & 1);
+    // ---- prologue: tiles t0, t0+1 and the Q fragments, then tile t0+2 in flight -----------
+    // The wait for Q is a compiler-visible s_waitcnt vmcnt(0) issued before tile t0+2: the
+    // compiler then knows Q is in registers and puts no wait of its own inside the loop (such a
+    // wait would also stall on the tiles in flight).
+    dma_tile(t_begin, true, 0);
+    dma_tile(t_begin + 1, t_begin + 1 < t_end, 1);
+    load_q();
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-
-    if (last) {
-      if (!more) break;
-      ++k;
-      bh = nbh;
-      q0 = nq0;
-      tb = ntb;
-      te = nte;
-      t = tb;
-      setup_wave(q0);
-      if constexpr (C::QLDS)
-        q_from_lds(k & 1);
-      else
-        q_from_global(bh);
-      reset();
-      rank_n = rank_of(k + 1);
-      more = rank_n < n_items;
-      if (more) decode(rank_n, nbh, nq0, ntb, nte);
-    } else {
-      ++t;
+#pragma unroll
+    for (int j = 2; j < C::PREFETCH; ++j) dma_tile(t_begin + j, t_begin + j < t_end, j);
+    f32x16 sacc[2][2];  // masked scores of the current tile and (being computed) of the next
+    {
+      float mx;
+      if (fast(t_begin)) {
+        scores(kslot(t_begin), t_begin, sacc[0], std::true_type{});
+        mx = mask_max(t_begin, sacc[0], std::true_type{});
+      } else {
+        scores(kslot(t_begin), t_begin, sacc[0], std::false_type{});
+        mx = mask_max(t_begin, sacc[0], std::false_type{});
+      }
+      decide(mx);
     }
-    slot ^= 1;
+
+    // ---- main loop -----------------------------------------------------------------------
+    // Iteration t: load tile t + PREFETCH into the stage tile t - 1 used (all reads of it ended
+    // before the previous barrier); scores of t+1 alongside the exponentials of t; P(t) V(t)
+    // alongside the mask and maximum of t+1; running-maximum update for t+1; wait until tile
+    // t+2 has landed; barrier.
+    auto body = [&](int t, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+      const bool has_next = t + 1 < t_end;
+      dma_tile(t + C::PREFETCH, t + C::PREFETCH < t_end, (t - t_begin + C::PREFETCH) % C::NSTAGE);
+      bf16x8 pf[2][2];
+      float mx = -INFINITY;
+      if (has_next && fast(t) && fast(t + 1)) {
+        scores(kslot(t + 1), t + 1, nxt, std::true_type{});
+        exps(cur, pf);
+        pv(vslot(t), t, pf, std::true_type{});
+        mx = mask_max(t + 1, nxt, std::true_type{});
+        // Phase A: the K fragment reads of t+1 go out first, then the score MFMAs of t+1
+        // alternate with the exponentials of t.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * C::KSTEPS, 0);
+#pragma unroll
+        for (int j = 0; j < 2 * C::KSTEPS; ++j) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 96 / (2 * C::KSTEPS), 0);
+        }
+        // Phase B: the P V MFMAs of t, each with its V reads issued two MFMAs ahead, alternate
+        // with the mask and maximum of t+1.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+        for (int j = 0; j < 4 * C::DB; ++j) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          if (j + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
+        }
+      } else {
+        if (has_next) scores(kslot(t + 1), t + 1, nxt, std::false_type{});
+        if (active(t, 0) || active(t, 1)) {
+          exps(cur, pf);
+          pv(vslot(t), t, pf, std::false_type{});
+        }
+        if (has_next) mx = mask_max(t + 1, nxt, std::false_type{});
+      }
+      if (has_next) decide(mx);
+      wait_vmcnt<(C::PREFETCH - 2) * C::DMA_PER_TILE>();  // tile t + 2 has landed
+      __syncthreads();
+    };
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+      body(t, sacc[0], sacc[1]);
+      body(t + 1, sacc[1], sacc[0]);
+    }
+    if (t < t_end) body(t, sacc[0], sacc[1]);
+  } else {
+    // ---- unpipelined: K and V one tile ahead; scores, softmax and P V of a tile in its own
+    // iteration --------------------------------------------------------------------------------
+    load_q();
+    {
+      u32x4 k0[C::LPT], v0[C::LPT];
+      gload(rk, t_begin, true, k0);
+      gload(rv, t_begin, true, v0);
+      lstore_k(0, k0);
+      lstore_v(0, v0);
+    }
+    __syncthreads();
+    u32x4 kst[C::LPT], vst[C::LPT];
+    for (int t = t_begin; t < t_end; ++t) {
+      const int i = t - t_begin;
+      gload(rk, t + 1, t + 1 < t_end, kst);
+      gload(rv, t + 1, t + 1 < t_end, vst);
+      if (active(t, 0) || active(t, 1)) {
+        f32x16 sa[2];
+        bf16x8 pf[2][2];
+        scores(i & 1, t, sa, std::false_type{});
+        decide(mask_max(t, sa, std::false_type{}));
+        exps(sa, pf);
+        pv(i & 1, t, pf, std::false_type{});
+      }
+      lstore_k((i + 1) & 1, kst);
+      lstore_v((i + 1) & 1, vst);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ------------------------------------
+  const float l_tot = pair_sum(l_run0 + l_run1);
+  if (qi < T) {
+    const float inv = 1.0f / l_tot;
+    bf16* orow = O + hoff + (int64_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w;
+      }
+    }
+    if (hi == 0 && LSE != nullptr) LSE[(int64_t)bh * T + qi] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
 template <int D, int MODE>
 static hipError_t launch_bf16_t(const void* q, const void* k, const void* v, void* out, float* lse,
                                 int B, int H, int T, int window, hipStream_t stream) {
-  // Workgroups the GPU holds at once, queried once per instantiation (a cache of a device
-  // property).
-  static int resident = 0;
-  if (resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<D, MODE>, 256, 0);
-    if (e != hipSuccess) return e;
-    resident = cus * (per_cu > 0 ? per_cu : 1);
-  }
   const int BH = B * H;
   const int nqt = (T + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
-  const int64_t n_items = (int64_t)BH * nqt;
-  const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
+  const unsigned grid = (unsigned)((int64_t)BH * nqt);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE>), dim3(grid), dim3(256), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, BH, T, window,
