@@ -278,7 +278,7 @@ def main() -> int:
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel<64>",
+            "kernel": "attn_fwd_bf16_stream<64, mode>",
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

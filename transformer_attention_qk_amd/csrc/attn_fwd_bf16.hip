@@ -9,40 +9,43 @@
 // describe the attention kernel they call only as a one-pass kernel with sub-quadratic memory;
 // the tiling and the one-pass (running maximum) softmax below are this library's design.
 //
-// Layout of the work:
-//   - A workgroup of 4 waves owns BM = 128 consecutive queries of one (batch, head); wave w owns
-//     queries [32w, 32w + 32) of that block. Workgroups are launched heaviest query block first
-//     (the last blocks of a causal head see the most keys).
-//   - Key/value tiles of BN = 64 rows flow HBM -> registers -> LDS through 2-slot LDS rings with
-//     one barrier per tile: V one tile ahead, K two tiles ahead when the loop is pipelined
-//     (below), else one.
+// Work split: items are (batch*head, block of BM = 128 queries); a workgroup of 4 waves owns one
+// item at a time, wave w owning queries [32w, 32w + 32) of the block. Per wave:
 //   - S^T = K Q^T per 32-key block with v_mfma_f32_32x32x16_bf16: A = K from LDS (16 bytes per
-//     lane), B = Q^T kept in registers for the whole workgroup. In the accumulator each lane owns
-//     one query (lane % 32) and 16 keys, so row maxima and sums are lane-local plus one exchange
+//     lane), B = Q^T kept in registers for the whole item. In the accumulator each lane owns one
+//     query (lane % 32) and 16 keys, so row maxima and sums are lane-local plus one exchange
 //     between lanes l and l + 32.
 //   - O^T += V^T P^T with the same MFMA: B = P^T straight from the S^T accumulator (rounded to
 //     bf16), A = V^T read from the row-major V tile with ds_read_b64_tr_b16, which transposes
 //     4x16 blocks of 16-bit values between lanes. The key order inside each 16-key MFMA step
 //     follows the S^T accumulator's register order on both operands.
-//   - Software pipeline inside each wave (d <= 64): the iteration for tile t issues the scores
-//     of tile t+1 on the matrix cores while the vector ALUs exponentiate tile t, then issues
-//     P(t) V(t) while the vector ALUs mask and reduce the scores of tile t+1. Unmasked tiles
-//     (the bulk) run this as one straight-line block with an explicit MFMA / VALU interleave.
 //   - Row sums of the weights are taken with v_dot2_f32_bf16 on the bf16-rounded weights, i.e.
 //     on exactly the values the P V product uses.
-//   - LDS rows are XOR-swizzled in 16-byte chunks so that the K reads (16 rows x 16 bytes per
-//     quarter-wave) and the transposing V reads (4 rows x 64 bytes per half-wave) hit distinct
-//     banks.
-//   - Tiles the mask hides completely are never loaded; 32-key blocks a wave cannot see are
-//     skipped by that wave; the elementwise mask is applied only on blocks that straddle the
-//     diagonal, the window edge or the end of the sequence.
-//   - Global loads are buffer loads whose range is the head's [T][d] slab: rows past T read as
-//     zero without a branch, and prefetches past the last tile are sent out of range, so every
-//     load and LDS store is unconditional and no prefetch is waited on before it is consumed.
 //   - The running maximum is raised lazily: only when a tile's maximum exceeds it by more than
 //     kRescaleSlack (base-2 units) are the accumulators rescaled. Until then the weights
 //     exp2(s - m) stay below 2^kRescaleSlack, which fp32 sums and bf16 weights hold exactly as
 //     well as weights below 1.
+//   - 32-key blocks a wave cannot see are skipped; the elementwise mask (a compile-time mode) is
+//     applied only on blocks that straddle the diagonal, the window edge or the sequence end.
+// LDS rows are XOR-swizzled in 16-byte chunks so that the K reads (16 rows x 16 bytes per
+// quarter-wave) and the transposing V reads (4 rows x 64 bytes per half-wave) hit distinct banks.
+//
+// Two kernels:
+//   - attn_fwd_bf16_stream (d <= 64): a persistent grid. Each workgroup walks a list of items
+//     ranked heaviest first (the last query blocks of a causal head see the most keys) and dealt
+//     out in snake order, and streams the K/V tiles of all its items through a 4-stage LDS ring
+//     with direct global -> LDS loads (buffer_load ... lds) three tiles ahead, across item
+//     boundaries. The next item's Q block arrives by the same route during the current item's
+//     last tile. Inside an item each wave runs a software pipeline: the scores of tile t+1 go to
+//     the matrix cores while the vector ALUs exponentiate tile t, then P(t) V(t) while the
+//     vector ALUs mask and reduce the scores of tile t+1, with an explicit MFMA / VALU
+//     interleave on unmasked tiles.
+//   - attn_fwd_bf16_tile (d = 128): one workgroup per item, K/V staged through registers one
+//     tile ahead. The pipelined form needs more registers than two waves per SIMD have at
+//     d = 128, where the matrix work per tile doubles while the softmax work stays the same.
+// Global loads are buffer loads whose range is the head's [T][d] slab: rows past T read as zero
+// without a branch, and loads of tiles that do not exist are sent out of range, so every load is
+// unconditional.
 #include <math.h>
 
 #include <type_traits>
@@ -54,7 +57,7 @@ namespace attn {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;             // queries per workgroup
+  static constexpr int BM = 128;             // queries per item
   static constexpr int BN = 64;              // keys per tile
   static constexpr int KSTEPS = D / 16;      // MFMA k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;          // 32-row blocks of O^T
@@ -62,18 +65,17 @@ struct FwdCfg {
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;
   static constexpr int LPT = BN * CH / 256;  // 16-byte chunks per thread per K or V tile
-  // Software-pipelined loop (two score accumulators live at once) fed by direct global -> LDS
-  // loads for d <= 64; at d = 128 that does not fit the registers of two waves per SIMD, and the
-  // matrix work per tile (twice that of d = 64 for the same softmax work) leaves the vector ALUs
-  // less to hide anyway.
-  static constexpr bool PIPE = D <= 64;
-  // Pipelined: a ring of NSTAGE (K tile, V tile) stages filled PREFETCH tiles ahead.
-  // Otherwise: K ring (2 tiles), then V ring (2 tiles), staged through registers.
+  static_assert(LPT >= 1, "tile too small for 256 threads");
+  // Streaming kernel: ring of NSTAGE (K tile, V tile) stages filled PREFETCH tiles ahead, then
+  // one Q block.
   static constexpr int NSTAGE = 4;
   static constexpr int PREFETCH = NSTAGE - 1;
-  static constexpr int LDS_BYTES = PIPE ? NSTAGE * 2 * TILE_BYTES : 4 * TILE_BYTES;
-  static constexpr int DMA_PER_TILE = 2 * LPT;  // direct loads per thread per (K, V) tile pair
-  static_assert(LPT >= 1, "tile too small for 256 threads");
+  static constexpr int Q_BYTES = BM * ROW_BYTES;
+  static constexpr int STREAM_LDS = NSTAGE * 2 * TILE_BYTES + Q_BYTES;
+  static constexpr int DMA_PER_TILE = 2 * LPT;             // direct loads per thread per stage
+  static constexpr int DMA_PER_Q = Q_BYTES / (1024 * 4);   // direct loads per thread per Q block
+  // Tile kernel: K ring (2 tiles), then V ring (2 tiles).
+  static constexpr int TILE_LDS = 4 * TILE_BYTES;
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row r of a K tile: quarter-wave K reads
@@ -172,129 +174,110 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt left unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Per-wave state and stages of one item (block of 128 queries of one head).
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int window_arg,
-    float scale_log2, int nqt) {
+struct WaveTile {
   using C = FwdCfg<D>;
-  constexpr bool causal = MODE != kNonCausal;
-  const int window = (MODE == kCausalWindow) ? window_arg : -1;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  static constexpr bool causal = MODE != kNonCausal;
+  int T, window, lane, l32, hi, wave;
+  float scale_log2;
+  // lane-constant LDS addressing. K (A operand of S^T): row 32 kb + l32, logical chunk
+  // 2 s + hi. V (A operand of O^T via the transposing read): lane (4a + b) of each 16-lane group
+  // addresses row k0 + a, columns 32 db + 16 g1 + 4 b .. +4, g1 = (lane / 16) % 2.
+  int k_row_off, k_swz, v_a, v_b, v_g1, v_swz;
+  // item: this wave's queries, the keys some of them see [w_lo, w_hi), the keys all of them see
+  // [f_lo, f_hi)
+  int qw0, qi, w_lo, w_hi, f_lo, f_hi;
+  bf16x8 qf[C::KSTEPS];  // Q^T fragments (B operand): Q[qi][16 s + 8 hi .. +8)
+  f32x16 oacc[C::DB];
+  float m_run, l_run0, l_run1;  // running max (base-2 units) and this lane's two partial sums
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-
-  const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest query block first
-  const int bh = (int)(blockIdx.x % BH);
-  const int64_t hoff = (int64_t)bh * T * D;
-  const int q0 = qt * C::BM;
-  const int qw0 = q0 + 32 * wave;
-  const int qi = qw0 + l32;  // the query this lane owns in S^T and O^T
-
-  const int slab = T * C::ROW_BYTES;  // bytes of one head's [T][d] slab (< 2^31, checked)
-  const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q + hoff, slab);
-  const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + hoff, slab);
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + hoff, slab);
-
-  // Keys any query of the workgroup sees: [kv_lo, kv_hi). Keys some query of this wave sees:
-  // [w_lo, w_hi); keys every query of the wave sees (no mask needed): [f_lo, f_hi).
-  int kv_lo = 0, kv_hi = T, w_lo = 0, w_hi = T, f_lo = 0, f_hi = T;
-  if constexpr (causal) {
-    kv_hi = min(T, q0 + C::BM);
-    w_hi = min(T, qw0 + 32);
-    f_hi = min(T, qw0 + 1);
-    if constexpr (MODE == kCausalWindow) {
-      kv_lo = max(0, q0 - window);
-      w_lo = max(0, qw0 - window);
-      f_lo = qw0 + 31 - window;
-    }
+  __device__ __forceinline__ void init(int T_, int window_, float scale_log2_, int tid) {
+    T = T_;
+    window = window_;
+    scale_log2 = scale_log2_;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    lane = tid & 63;
+    l32 = lane & 31;
+    hi = lane >> 5;
+    k_row_off = l32 * C::ROW_BYTES;
+    k_swz = swz_k<D>(l32);
+    v_a = (lane & 15) >> 2;
+    v_b = lane & 3;
+    v_g1 = (lane >> 4) & 1;
+    v_swz = swz_v<D>(v_a);  // row = (multiple of 4) + v_a, so the swizzle is lane-constant
   }
-  const int t_begin = kv_lo / C::BN;
-  const int t_end = (kv_hi + C::BN - 1) / C::BN;
-  auto active = [&](int t, int kb) {
+  __device__ __forceinline__ void set_item(int q0) {
+    qw0 = q0 + 32 * wave;
+    qi = qw0 + l32;
+    w_lo = 0;
+    w_hi = T;
+    f_lo = 0;
+    f_hi = T;
+    if constexpr (causal) {
+      w_hi = min(T, qw0 + 32);
+      f_hi = min(T, qw0 + 1);
+      if constexpr (MODE == kCausalWindow) {
+        w_lo = max(0, qw0 - window);
+        f_lo = qw0 + 31 - window;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+    m_run = -INFINITY;
+    l_run0 = 0.f;
+    l_run1 = 0.f;
+  }
+  __device__ __forceinline__ bool active(int t, int kb) const {
     const int b0 = t * C::BN + 32 * kb;
     return (b0 < w_hi) && (b0 + 32 > w_lo);
-  };
-  auto full = [&](int t, int kb) {
+  }
+  __device__ __forceinline__ bool full(int t, int kb) const {
     const int b0 = t * C::BN + 32 * kb;
     return (b0 >= f_lo) && (b0 + 32 <= f_hi);
-  };
-  auto fast = [&](int t) { return full(t, 0) && full(t, 1); };
+  }
+  // (bitwise operators: the operands are cheap scalar tests, evaluated without branches)
+  __device__ __forceinline__ bool fast(int t) const { return full(t, 0) & full(t, 1); }
+  __device__ __forceinline__ bool any(int t) const { return active(t, 0) | active(t, 1); }
+  // Tiles t and t + 1 both fully visible to all of this wave's queries.
+  __device__ __forceinline__ bool fast2(int t) const {
+    return (t * C::BN >= f_lo) & (t * C::BN + 2 * C::BN <= f_hi);
+  }
 
-  // Q^T fragments (B operand): lane holds Q[qi][16 s + 8 hi .. +8); rows past T read as zero.
-  bf16x8 qf[C::KSTEPS];
-  auto load_q = [&]() {
+  __device__ __forceinline__ void q_from_global(__amdgpu_buffer_rsrc_t rq) {
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
       qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qi * C::ROW_BYTES + 32 * s + 16 * hi)));
-  };
-
-  // ---- global -> register staging, LDS stores ---------------------------------------------
-  auto gload = [&](__amdgpu_buffer_rsrc_t r, int t, bool needed, u32x4(&st)[C::LPT]) {
+  }
+  // Q block staged in LDS with the K layout: wave w reads rows 32 w + l32 (the swizzle of those
+  // rows equals that of l32).
+  __device__ __forceinline__ void q_from_lds(const char* qbuf) {
+    const char* qb = qbuf + 32 * wave * C::ROW_BYTES + k_row_off;
 #pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      const int e = tid + 256 * u;
-      const uint32_t off =
-          needed ? (uint32_t)((t * C::BN + e / C::CH) * C::ROW_BYTES + 16 * (e % C::CH)) : kOutOfRange;
-      st[u] = buffer_load16(r, off);
-    }
-  };
-  auto lstore_k = [&](int slot, const u32x4(&st)[C::LPT]) {
-    char* base = smem + slot * C::TILE_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e / C::CH, c = e % C::CH;
-      *reinterpret_cast<u32x4*>(base + r * C::ROW_BYTES + 16 * (c ^ swz_k<D>(r))) = st[u];
-    }
-  };
-  auto lstore_v = [&](int slot, const u32x4(&st)[C::LPT]) {
-    char* base = smem + (2 + slot) * C::TILE_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e / C::CH, c = e % C::CH;
-      *reinterpret_cast<u32x4*>(base + r * C::ROW_BYTES + 16 * (c ^ swz_v<D>(r))) = st[u];
-    }
-  };
+    for (int s = 0; s < C::KSTEPS; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8*>(qb + 16 * ((2 * s + hi) ^ k_swz));
+  }
 
-  // Lane-constant parts of the LDS read addresses.
-  // K (A operand of S^T): row 32 kb + l32, logical chunk 2 s + hi.
-  const int k_row_off = l32 * C::ROW_BYTES;
-  const int k_swz = swz_k<D>(l32);
-  // V (A operand of O^T via the transposing read): lane (4a + b) of each 16-lane group addresses
-  // row k0 + a, columns 32 db + 16 g1 + 4 b .. +4, where g1 = (lane / 16) % 2.
-  const int v_a = (lane & 15) >> 2;
-  const int v_b = lane & 3;
-  const int v_g1 = (lane >> 4) & 1;
-  const int v_swz = swz_v<D>(v_a);  // row = (multiple of 4) + v_a, so the swizzle is lane-constant
-
-  // ---- stages of a tile ---------------------------------------------------------------------
-  // Scores of tile t (K from ring slot `slot`) for the blocks this wave sees.
-  auto scores = [&](int slot, int t, f32x16(&sa)[2], auto fast_tag) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    const char* kb_base = smem + slot * C::TILE_BYTES;
+  // Scores of tile t (K tile at kbuf) for the blocks this wave sees. INTERLEAVE runs the two
+  // accumulation chains side by side (more independent work, more K fragments in flight).
+  template <bool FAST, bool INTERLEAVE>
+  __device__ __forceinline__ void scores(const char* kbuf, int t, f32x16 (&sa)[2]) {
     const bool a0 = FAST || active(t, 0), a1 = FAST || active(t, 1);
-    if (a0) sa[0] = f32x16{};
-    if (a1) sa[1] = f32x16{};
+    // Both accumulators are defined on every path, so no earlier value stays live through here.
+    sa[0] = f32x16{};
+    sa[1] = f32x16{};
     auto step = [&](int s, int kb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + 32 * kb * C::ROW_BYTES +
-                                                        k_row_off + 16 * ((2 * s + hi) ^ k_swz));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + 32 * kb * C::ROW_BYTES + k_row_off +
+                                                        16 * ((2 * s + hi) ^ k_swz));
       sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sa[kb], 0, 0, 0);
     };
-    if constexpr (C::PIPE) {
-      // the two accumulation chains interleaved
+    if constexpr (INTERLEAVE) {
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         if (a0) step(s, 0);
         if (a1) step(s, 1);
       }
     } else {
-      // one block after the other keeps fewer K fragments in flight (register budget at d=128)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (!(kb == 0 ? a0 : a1)) continue;
@@ -302,11 +285,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         for (int s = 0; s < C::KSTEPS; ++s) step(s, kb);
       }
     }
-  };
+  }
 
   // Mask the scores of tile t and return their row maximum (raw, pair-reduced).
-  auto mask_max = [&](int t, f32x16(&sa)[2], auto fast_tag) -> float {
-    constexpr bool FAST = decltype(fast_tag)::value;
+  template <bool FAST>
+  __device__ __forceinline__ float mask_max(int t, f32x16 (&sa)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (!FAST) {
@@ -343,16 +326,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const float m2a = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
     const float m2b = fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7]));
     return pair_max(fmaxf(m2a, m2b));
-  };
-
-  f32x16 oacc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;           // running maximum of the scaled scores, base-2 units
-  float l_run0 = 0.f, l_run1 = 0.f;  // this lane's part of the running sum (two chains)
+  }
 
   // Lazy running-maximum update with a tile's row maximum (raw scores).
-  auto decide = [&](float mx) {
+  __device__ __forceinline__ void decide(float mx) {
     const float m_tile = mx * scale_log2;
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
@@ -365,11 +342,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-  };
+  }
 
   // P = exp2(s * scale - m), rounded to bf16 in the B-operand order of the P V product; the row
   // sums add the rounded values.
-  auto exps = [&](const f32x16(&sa)[2], bf16x8(&pf)[2][2]) {
+  __device__ __forceinline__ void exps(const f32x16 (&sa)[2], bf16x8 (&pf)[2][2]) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -389,12 +366,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         pf[kb][tt] = __builtin_bit_cast(bf16x8, w);
       }
     }
-  };
+  }
 
-  // O^T += V^T P^T for tile t (V from ring slot `slot`).
-  auto pv = [&](int slot, int t, const bf16x8(&pf)[2][2], auto fast_tag) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    const char* vb = smem + (2 + slot) * C::TILE_BYTES;
+  // O^T += V^T P^T for tile t (V tile at vbuf).
+  template <bool FAST>
+  __device__ __forceinline__ void pv(const char* vbuf, int t, const bf16x8 (&pf)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (!FAST) {
@@ -409,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
           for (int u = 0; u < 2; ++u) {
             const int row = 32 * kb + 16 * tt + 8 * u + 4 * hi + v_a;
             const int c = 4 * db + 2 * v_g1 + (v_b >> 1);
-            part[u] = ds_read_tr16_b64(vb + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
+            part[u] = ds_read_tr16_b64(vbuf + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
           }
           const u32x4 a4{part[0][0], part[0][1], part[1][0], part[1][1]};
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
@@ -417,72 +393,190 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         }
       }
     }
+  }
+
+  // Unpipelined tile: scores, mask and maximum, update, exponentials, P V.
+  __device__ __forceinline__ void whole_tile(const char* kbuf, const char* vbuf, int t) {
+    f32x16 sa[2];
+    bf16x8 pf[2][2];
+    scores<false, false>(kbuf, t, sa);
+    decide(mask_max<false>(t, sa));
+    exps(sa, pf);
+    pv<false>(vbuf, t, pf);
+  }
+
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 for this wave's queries of head offset hoff.
+  __device__ __forceinline__ void store(bf16* O, float* LSE, int64_t hoff, int64_t lse_off) {
+    const float l_tot = pair_sum(l_run0 + l_run1);
+    if (qi < T) {
+      const float inv = 1.0f / l_tot;
+      bf16* orow = O + hoff + (int64_t)qi * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w;
+        }
+      }
+      if (hi == 0 && LSE != nullptr) LSE[lse_off + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+  }
+};
+
+// Key range [lo, up) of an item's query block and its tile range [tb, te).
+template <int D, int MODE>
+__device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, int& te) {
+  using C = FwdCfg<D>;
+  int lo = 0, up = T;
+  if constexpr (MODE != kNonCausal) {
+    up = min(T, q0 + C::BM);
+    if constexpr (MODE == kCausalWindow) lo = max(0, q0 - window);
+  }
+  tb = lo / C::BN;
+  te = (up + C::BN - 1) / C::BN;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Streaming kernel (d <= 64): persistent grid, direct-to-LDS K/V stream, pipelined tiles.
+// ---------------------------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int window_arg,
+    float scale_log2, int nqt) {
+  using C = FwdCfg<D>;
+  const int window = (MODE == kCausalWindow) ? window_arg : -1;
+  __shared__ __attribute__((aligned(16))) char smem[C::STREAM_LDS];
+  const int tid = threadIdx.x;
+  WaveTile<D, MODE> w;
+  w.init(T, window, scale_log2, tid);
+  const int P = (int)gridDim.x;
+  const int g = (int)blockIdx.x;
+  const int n_items = BH * nqt;
+  const int slab = T * C::ROW_BYTES;  // bytes of one head's [T][d] slab (< 2^31, checked)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+  const char* qbuf = smem + C::NSTAGE * 2 * C::TILE_BYTES;
+
+  // Items of this workgroup: heaviest-first ranks dealt out in snake order.
+  auto rank_of = [&](int k) { return k * P + ((k & 1) ? (P - 1 - g) : g); };
+  auto decode = [&](int rank, int& bh, int& q0, int& tb, int& te) {
+    bh = rank % BH;
+    q0 = (nqt - 1 - rank / BH) * C::BM;
+    item_tiles<D, MODE>(q0, T, window, tb, te);
   };
 
-  if constexpr (C::PIPE) {
-    // Stage st holds a K tile then a V tile; tile t lives in stage (t - t0) % NSTAGE.
-    const u32x4 rk_w = head_rsrc_words(K + hoff, slab);
-    const u32x4 rv_w = head_rsrc_words(V + hoff, slab);
-    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
-    // Issue the direct loads of tile t (out of range when not needed) into stage st. Wave w
-    // fills 1 KiB runs (w * LPT + u) of each tile; lane L of a run writes chunk p = run * 64 + L,
-    // i.e. row p / CH at physical chunk p % CH, so it loads the logical chunk that the row's
-    // swizzle puts there.
-    auto dma_tile = [&](int t, bool needed, int st) {
-      const uint32_t kb_ = lds0 + st * 2 * C::TILE_BYTES;
-      const uint32_t vb_ = kb_ + C::TILE_BYTES;
+  // Offsets of this lane's 16-byte chunks inside a K and a V tile: lane L of run
+  // (wave * LPT + u) fills chunk p = run * 64 + L of the tile, i.e. row p / CH at physical chunk
+  // p % CH, so it loads the logical chunk the row's swizzle puts there.
+  uint32_t kofs[C::LPT], vofs[C::LPT];
 #pragma unroll
-      for (int u = 0; u < C::LPT; ++u) {
-        const int run = wave * C::LPT + u;
-        const int p = run * 64 + lane;
-        const int r = p / C::CH, pc = p % C::CH;
-        const uint32_t row_off = (uint32_t)((t * C::BN + r) * C::ROW_BYTES);
-        dma16(rk_w, kb_ + run * 1024, needed ? row_off + 16 * (pc ^ swz_k<D>(r)) : kOutOfRange);
-        dma16(rv_w, vb_ + run * 1024, needed ? row_off + 16 * (pc ^ swz_v<D>(r)) : kOutOfRange);
-      }
-    };
-    auto kslot = [&](int t) { return 2 * ((t - t_begin) % C::NSTAGE); };      // K ring slot
-    auto vslot = [&](int t) { return 2 * ((t - t_begin) % C::NSTAGE) - 1; };  // V, as pv() adds 2
-
-    // ---- prologue: tiles t0, t0+1 and the Q fragments, then tile t0+2 in flight -----------
-    // The wait for Q is a compiler-visible s_waitcnt vmcnt(0) issued before tile t0+2: the
-    // compiler then knows Q is in registers and puts no wait of its own inside the loop (such a
-    // wait would also stall on the tiles in flight).
-    dma_tile(t_begin, true, 0);
-    dma_tile(t_begin + 1, t_begin + 1 < t_end, 1);
-    load_q();
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+  for (int u = 0; u < C::LPT; ++u) {
+    const unsigned p = (unsigned)((w.wave * C::LPT + u) * 64 + w.lane);
+    const unsigned r = p / C::CH, pc = p % C::CH;
+    kofs[u] = r * C::ROW_BYTES + 16 * (pc ^ swz_k<D>((int)r));
+    vofs[u] = r * C::ROW_BYTES + 16 * (pc ^ swz_v<D>((int)r));
+  }
+  // Direct loads of the Q block of an item into the Q buffer (K layout).
+  auto dma_q = [&](int bh, int q0) {
+    const u32x4 rq = head_rsrc_words(Q + (int64_t)bh * T * D, slab);
+    const uint32_t qb_ = lds0 + C::NSTAGE * 2 * C::TILE_BYTES;
 #pragma unroll
-    for (int j = 2; j < C::PREFETCH; ++j) dma_tile(t_begin + j, t_begin + j < t_end, j);
-    f32x16 sacc[2][2];  // masked scores of the current tile and (being computed) of the next
-    {
-      float mx;
-      if (fast(t_begin)) {
-        scores(kslot(t_begin), t_begin, sacc[0], std::true_type{});
-        mx = mask_max(t_begin, sacc[0], std::true_type{});
-      } else {
-        scores(kslot(t_begin), t_begin, sacc[0], std::false_type{});
-        mx = mask_max(t_begin, sacc[0], std::false_type{});
-      }
-      decide(mx);
+    for (int u = 0; u < C::DMA_PER_Q; ++u) {
+      const unsigned run = (unsigned)(w.wave * C::DMA_PER_Q + u);
+      const unsigned p = run * 64 + (unsigned)w.lane;
+      const unsigned r = p / C::CH, pc = p % C::CH;
+      dma16(rq, qb_ + run * 1024, ((unsigned)q0 + r) * C::ROW_BYTES + 16 * (pc ^ swz_k<D>((int)r)));
     }
+  };
 
-    // ---- main loop -----------------------------------------------------------------------
-    // Iteration t: load tile t + PREFETCH into the stage tile t - 1 used (all reads of it ended
+  // The K/V stream: one tile per step, across items. The cursor holds the next tile to issue
+  // (pt of [pt, pte) of the item of rank index pk), that head's K and V buffer resources and the
+  // stage the tile goes to. Once the items run out, out-of-range loads keep the count per step
+  // (and so the waits) the same.
+  int pk = 0, pt = 0, pte = 0;
+  bool pvalid = true;
+  u32x4 prk, prv;
+  unsigned st_issue = 0;
+  auto seek = [&](int rank) {
+    int bh_, q0_;
+    decode(rank, bh_, q0_, pt, pte);
+    const int64_t hoff = (int64_t)bh_ * T * D;
+    prk = head_rsrc_words(K + hoff, slab);
+    prv = head_rsrc_words(V + hoff, slab);
+  };
+  seek(rank_of(0));  // g < P <= n_items
+  auto issue_next = [&]() {
+    const uint32_t kb_ = lds0 + st_issue * (2 * C::TILE_BYTES) + w.wave * (C::LPT * 1024);
+    const uint32_t vb_ = kb_ + C::TILE_BYTES;
+    const uint32_t base = pvalid ? (uint32_t)(pt * C::TILE_BYTES) : kOutOfRange;
+#pragma unroll
+    for (int u = 0; u < C::LPT; ++u) {
+      dma16(prk, kb_ + u * 1024, base + kofs[u]);
+      dma16(prv, vb_ + u * 1024, base + vofs[u]);
+    }
+    st_issue = (st_issue + 1) & (C::NSTAGE - 1);
+    if (pvalid && ++pt >= pte) {
+      const int r = rank_of(++pk);
+      pvalid = r < n_items;
+      if (pvalid) seek(r);
+    }
+  };
+
+  // Workgroup prologue: stream tiles 0 and 1 and the first item's Q, then tile 2 in flight. The
+  // wait for Q is a compiler-visible s_waitcnt vmcnt(0), so the compiler puts no wait of its own
+  // inside the loop (such a wait would also stall on the tiles in flight).
+  int k = 0, bh, q0, tb, te;
+  decode(rank_of(0), bh, q0, tb, te);
+  w.set_item(q0);
+  issue_next();
+  issue_next();
+  w.q_from_global(head_rsrc(Q + (int64_t)bh * T * D, slab));
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  issue_next();
+  unsigned st_comp = 0;  // stage of the tile being consumed
+
+  while (true) {
+    // Item prologue: scores, mask and maximum of its first tile.
+    f32x16 sacc[2][2];
+    {
+      const char* kb0 = smem + st_comp * (2 * C::TILE_BYTES);
+      float mx;
+      if (w.fast(tb)) {
+        w.template scores<true, true>(kb0, tb, sacc[0]);
+        mx = w.template mask_max<true>(tb, sacc[0]);
+      } else {
+        w.template scores<false, true>(kb0, tb, sacc[0]);
+        mx = w.template mask_max<false>(tb, sacc[0]);
+      }
+      w.decide(mx);
+    }
+    const int rank_n = rank_of(k + 1);
+    const bool more = rank_n < n_items;
+    int nbh = 0, nq0 = 0, ntb = 0, nte = 0;
+    if (more) decode(rank_n, nbh, nq0, ntb, nte);
+
+    // Tile t: the next stream tile is issued into the stage tile t-1 used (all reads of it ended
     // before the previous barrier); scores of t+1 alongside the exponentials of t; P(t) V(t)
-    // alongside the mask and maximum of t+1; running-maximum update for t+1; wait until tile
-    // t+2 has landed; barrier.
+    // alongside the mask and maximum of t+1; running-maximum update; wait until the stream tile
+    // two ahead has landed; barrier. The item's last tile also fetches the next item's Q block,
+    // issued before the stream tile so the same wait covers it.
     auto body = [&](int t, f32x16(&cur)[2], f32x16(&nxt)[2]) {
-      const bool has_next = t + 1 < t_end;
-      dma_tile(t + C::PREFETCH, t + C::PREFETCH < t_end, (t - t_begin + C::PREFETCH) % C::NSTAGE);
+      const bool has_next = t + 1 < te;
+      if (!has_next && more) dma_q(nbh, nq0);
+      issue_next();
+      const char* kn = smem + ((st_comp + 1) & (C::NSTAGE - 1)) * (2 * C::TILE_BYTES);
+      const char* vc = smem + st_comp * (2 * C::TILE_BYTES) + C::TILE_BYTES;
       bf16x8 pf[2][2];
       float mx = -INFINITY;
-      if (has_next && fast(t) && fast(t + 1)) {
-        scores(kslot(t + 1), t + 1, nxt, std::true_type{});
-        exps(cur, pf);
-        pv(vslot(t), t, pf, std::true_type{});
-        mx = mask_max(t + 1, nxt, std::true_type{});
+      if (w.fast2(t)) {
+        w.template scores<true, true>(kn, t + 1, nxt);
+        w.exps(cur, pf);
+        w.template pv<true>(vc, t, pf);
+        mx = w.template mask_max<true>(t + 1, nxt);
         // Phase A: the K fragment reads of t+1 go out first, then the score MFMAs of t+1
         // alternate with the exponentials of t.
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * C::KSTEPS, 0);
@@ -501,71 +595,129 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
           __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
         }
       } else {
-        if (has_next) scores(kslot(t + 1), t + 1, nxt, std::false_type{});
-        if (active(t, 0) || active(t, 1)) {
-          exps(cur, pf);
-          pv(vslot(t), t, pf, std::false_type{});
+        if (has_next) w.template scores<false, true>(kn, t + 1, nxt);
+        if (w.any(t)) {
+          w.exps(cur, pf);
+          w.template pv<false>(vc, t, pf);
         }
-        if (has_next) mx = mask_max(t + 1, nxt, std::false_type{});
+        if (has_next) mx = w.template mask_max<false>(t + 1, nxt);
       }
-      if (has_next) decide(mx);
-      wait_vmcnt<(C::PREFETCH - 2) * C::DMA_PER_TILE>();  // tile t + 2 has landed
+      if (has_next) w.decide(mx);
+      wait_vmcnt<(C::PREFETCH - 2) * C::DMA_PER_TILE>();  // the tile two stages ahead has landed
       __syncthreads();
+      st_comp = (st_comp + 1) & (C::NSTAGE - 1);
     };
-    int t = t_begin;
-    for (; t + 1 < t_end; t += 2) {
+    int t = tb;
+    for (; t + 1 < te; t += 2) {
       body(t, sacc[0], sacc[1]);
       body(t + 1, sacc[1], sacc[0]);
     }
-    if (t < t_end) body(t, sacc[0], sacc[1]);
-  } else {
-    // ---- unpipelined: K and V one tile ahead; scores, softmax and P V of a tile in its own
-    // iteration --------------------------------------------------------------------------------
-    load_q();
-    {
-      u32x4 k0[C::LPT], v0[C::LPT];
-      gload(rk, t_begin, true, k0);
-      gload(rv, t_begin, true, v0);
-      lstore_k(0, k0);
-      lstore_v(0, v0);
-    }
-    __syncthreads();
-    u32x4 kst[C::LPT], vst[C::LPT];
-    for (int t = t_begin; t < t_end; ++t) {
-      const int i = t - t_begin;
-      gload(rk, t + 1, t + 1 < t_end, kst);
-      gload(rv, t + 1, t + 1 < t_end, vst);
-      if (active(t, 0) || active(t, 1)) {
-        f32x16 sa[2];
-        bf16x8 pf[2][2];
-        scores(i & 1, t, sa, std::false_type{});
-        decide(mask_max(t, sa, std::false_type{}));
-        exps(sa, pf);
-        pv(i & 1, t, pf, std::false_type{});
-      }
-      lstore_k((i + 1) & 1, kst);
-      lstore_v((i + 1) & 1, vst);
-      __syncthreads();
-    }
-  }
+    if (t < te) body(t, sacc[0], sacc[1]);
 
-  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 ------------------------------------
-  const float l_tot = pair_sum(l_run0 + l_run1);
-  if (qi < T) {
-    const float inv = 1.0f / l_tot;
-    bf16* orow = O + hoff + (int64_t)qi * D;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w;
-      }
+    // Item epilogue, after the barrier so the stores do not sit between a stream tile's loads
+    // and the wait for them.
+    w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
+    if (!more) {
+      // The stream's last loads (out of range, writing zeros) land before the workgroup's LDS
+      // is released.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      break;
     }
-    if (hi == 0 && LSE != nullptr) LSE[(int64_t)bh * T + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    ++k;
+    bh = nbh;
+    q0 = nq0;
+    tb = ntb;
+    te = nte;
+    w.set_item(q0);
+    w.q_from_lds(qbuf);
+    // Every wave has its Q fragments before anyone issues the next Q block into the buffer.
+    __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Tile kernel (d = 128): one workgroup per item, K/V staged through registers one tile ahead.
+// ---------------------------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int window_arg,
+    float scale_log2, int nqt) {
+  using C = FwdCfg<D>;
+  const int window = (MODE == kCausalWindow) ? window_arg : -1;
+  __shared__ __attribute__((aligned(16))) char smem[C::TILE_LDS];
+  const int tid = threadIdx.x;
+  WaveTile<D, MODE> w;
+  w.init(T, window, scale_log2, tid);
+  const int bh = (int)(blockIdx.x % BH);
+  const int q0 = (nqt - 1 - (int)(blockIdx.x / BH)) * C::BM;  // heaviest query block first
+  const int64_t hoff = (int64_t)bh * T * D;
+  const int slab = T * C::ROW_BYTES;
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + hoff, slab);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + hoff, slab);
+  int tb, te;
+  item_tiles<D, MODE>(q0, T, window, tb, te);
+  w.set_item(q0);
+  w.q_from_global(head_rsrc(Q + hoff, slab));
+
+  auto gload = [&](__amdgpu_buffer_rsrc_t r, int t, bool needed, u32x4(&st)[C::LPT]) {
+#pragma unroll
+    for (int u = 0; u < C::LPT; ++u) {
+      const int e = tid + 256 * u;
+      const uint32_t off =
+          needed ? (uint32_t)((t * C::BN + e / C::CH) * C::ROW_BYTES + 16 * (e % C::CH)) : kOutOfRange;
+      st[u] = buffer_load16(r, off);
+    }
+  };
+  auto lstore = [&](int slot, const u32x4(&ks)[C::LPT], const u32x4(&vs)[C::LPT]) {
+    char* kb_ = smem + slot * C::TILE_BYTES;
+    char* vb_ = smem + (2 + slot) * C::TILE_BYTES;
+#pragma unroll
+    for (int u = 0; u < C::LPT; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / C::CH, c = e % C::CH;
+      *reinterpret_cast<u32x4*>(kb_ + r * C::ROW_BYTES + 16 * (c ^ swz_k<D>(r))) = ks[u];
+      *reinterpret_cast<u32x4*>(vb_ + r * C::ROW_BYTES + 16 * (c ^ swz_v<D>(r))) = vs[u];
+    }
+  };
+
+  u32x4 kst[C::LPT], vst[C::LPT];
+  gload(rk, tb, true, kst);
+  gload(rv, tb, true, vst);
+  lstore(0, kst, vst);
+  __syncthreads();
+  for (int t = tb; t < te; ++t) {
+    const int i = t - tb;
+    gload(rk, t + 1, t + 1 < te, kst);
+    gload(rv, t + 1, t + 1 < te, vst);
+    if (w.any(t)) w.whole_tile(smem + (i & 1) * C::TILE_BYTES, smem + (2 + (i & 1)) * C::TILE_BYTES, t);
+    lstore((i + 1) & 1, kst, vst);
+    __syncthreads();
+  }
+  w.store(O, LSE, hoff, (int64_t)bh * T);
+}
+
+// Workgroups of a kernel the current device holds at once (cached per device and
+// instantiation; a benign race between threads writes the same value).
+template <typename Kern>
+static hipError_t resident_workgroups(Kern kern, int* out) {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && cached[dev] > 0) {
+    *out = cached[dev];
+    return hipSuccess;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+  if (e != hipSuccess) return e;
+  const int n = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  if (dev >= 0 && dev < kMaxDevices) cached[dev] = n;
+  *out = n;
+  return hipSuccess;
 }
 
 template <int D, int MODE>
@@ -573,11 +725,21 @@ static hipError_t launch_bf16_t(const void* q, const void* k, const void* v, voi
                                 int B, int H, int T, int window, hipStream_t stream) {
   const int BH = B * H;
   const int nqt = (T + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
-  const unsigned grid = (unsigned)((int64_t)BH * nqt);
+  const int64_t n_items = (int64_t)BH * nqt;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MODE>), dim3(grid), dim3(256), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, BH, T, window,
-                     scale_log2, nqt);
+  if constexpr (D <= 64) {
+    int resident = 0;
+    hipError_t e = resident_workgroups(attn_fwd_bf16_stream<D, MODE>, &resident);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
+    hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE>), dim3(grid), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, BH, T,
+                       window, scale_log2, nqt);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE>), dim3((unsigned)n_items), dim3(256), 0,
+                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, BH,
+                       T, window, scale_log2, nqt);
+  }
   return hipGetLastError();
 }
 
