@@ -3,17 +3,19 @@
 forward) on one MI355X.
 
 One step is one pass of the whole path over one batch of synthetic input: for each layer of the
-ANDREA-120M SSSL stack (B=16, H=12, T=1024, d=64, bf16; windows 512, 512, 512, 1024), the fused
-QK-RMSNorm + RoPE prologue on that layer's q and k, then the attention forward with that
-layer's window. Inputs are resident in HBM before timing starts; every layer has its own
-buffers.
+ANDREA-120M SSSL stack (B=16, H=12, T=1024, d=64, bf16; windows 512, 512, 512, 1024),
+QK-RMSNorm + RoPE of that layer's raw q and k and the attention forward with that layer's
+window, through the library's one-call layer entry point (attn_fwd_qknorm: a k-only
+norm + rotation kernel, then the attention kernel that normalises and rotates q as it loads
+it). Inputs are resident in HBM before timing starts; every layer has its own buffers. The
+two-call path (attn_qknorm_rope on q and k, then attn_fwd) is timed too and reported beside it.
 
 The value is counted the way the metric names it: TFLOP/s of unmasked attention work
 (4 d FLOPs per visible (query, key) pair) over the whole step's time, prologue included.
 It prints ONE JSON line on stdout.
 
 Extra modes (used to collect rocprofv3 counters; they print no JSON):
-  --only attn|prologue   run only that kernel, --steps times, after the inputs are ready
+  --only attn|kprologue|attn_unfused|prologue   run only that kernel, --steps times per layer
   --copy-calibration     run a plain 256 MiB device copy (known bytes) for counter scaling
 """
 
@@ -57,9 +59,10 @@ def attn_compulsory_bytes(B: int, H: int, T: int, d: int, elem: int = 2) -> int:
     return B * H * T * (4 * d * elem + 4)
 
 
-def prologue_bytes(B: int, H: int, T: int, d: int, elem: int = 2) -> int:
-    """HBM bytes of one prologue launch: q, k read and written (the RoPE table is cached)."""
-    return B * H * T * 4 * d * elem
+def prologue_bytes(B: int, H: int, T: int, d: int, elem: int = 2, tensors: int = 2) -> int:
+    """HBM bytes of one prologue launch: each of `tensors` (q and k, or k alone) read and
+    written once (the RoPE table is cached)."""
+    return B * H * T * 2 * tensors * d * elem
 
 
 def source_sha(path: str) -> str:
@@ -133,7 +136,8 @@ def main() -> int:
     ap.add_argument("--workload", default="andrea120m_sssl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
-    ap.add_argument("--only", choices=["attn", "prologue"], default=None)
+    ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue"],
+                    default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -188,22 +192,40 @@ def main() -> int:
     eps = 1e-6
     torch.cuda.synchronize()
 
+    # The layer as one call, and its two kernels as separate calls (the same launches).
+    def layer(l):
+        ops.attn_fwd_qknorm(q[l], k[l], v[l], cos, sin, window=windows[l], eps=eps, k_work=kn[l],
+                            out=out[l], lse=lse[l])
+
+    def kprologue(l):
+        ops.qknorm_rope(None, k[l], cos, sin, eps, k_out=kn[l])
+
+    def attention(l):
+        ops.attn_fwd_qnorm(q[l], kn[l], v[l], cos, sin, window=windows[l], eps=eps, out=out[l],
+                           lse=lse[l])
+
+    # The two-call path.
     def prologue(l):
         ops.qknorm_rope(q[l], k[l], cos, sin, eps, q_out=qn[l], k_out=kn[l])
 
-    def attention(l):
+    def attention_unfused(l):
         ops.attn_fwd(qn[l], kn[l], v[l], window=windows[l], out=out[l], lse=lse[l])
 
     def step():
         for l in range(L):
+            layer(l)
+
+    def step_unfused():
+        for l in range(L):
             prologue(l)
-            attention(l)
+            attention_unfused(l)
 
     if args.only:
         for l in range(L):
             prologue(l)
         torch.cuda.synchronize()
-        fn = attention if args.only == "attn" else prologue
+        fn = {"attn": attention, "kprologue": kprologue, "attn_unfused": attention_unfused,
+              "prologue": prologue}[args.only]
         for _ in range(args.steps):
             for l in range(L):
                 fn(l)
@@ -211,42 +233,49 @@ def main() -> int:
         print(f"ran {args.only} x {args.steps * L}", file=sys.stderr)
         return 0
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def time_steps(fn) -> float:
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
-    # Timed region 1: whole steps, nothing between the kernels.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    def time_launches(first, second) -> tuple[list[float], list[float]]:
+        """Per-layer average ms of two back-to-back launches, HIP events around each (the
+        kernels run on torch's current stream, where the events are recorded)."""
+        ev = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(L)]
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s_ in range(args.steps):
+            for l in range(L):
+                a_, b_, c_ = ev[s_][l]
+                a_.record()
+                first(l)
+                b_.record()
+                second(l)
+                c_.record()
+        torch.cuda.synchronize()
+        t1, t2 = [0.0] * L, [0.0] * L
+        for s_ in range(args.steps):
+            for l in range(L):
+                a_, b_, c_ = ev[s_][l]
+                t1[l] += a_.elapsed_time(b_) / args.steps
+                t2[l] += b_.elapsed_time(c_) / args.steps
+        return t1, t2
 
-    # Timed region 2: the same steps with HIP events around every launch (the kernels run on
-    # torch's current stream, which is where the events are recorded).
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(L)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        for l in range(L):
-            a, b, c = ev[s][l]
-            a.record()
-            prologue(l)
-            b.record()
-            attention(l)
-            c.record()
-    torch.cuda.synchronize()
-    attn_ms = [0.0] * L
-    pro_ms = [0.0] * L
-    for s in range(args.steps):
-        for l in range(L):
-            a, b, c = ev[s][l]
-            pro_ms[l] += a.elapsed_time(b) / args.steps
-            attn_ms[l] += b.elapsed_time(c) / args.steps
+    # Timed region 1: whole steps, nothing between the kernels (the value).
+    ms_per_step = time_steps(step)
+    # Timed region 2: the same launches with events around each kernel (the roofline).
+    kpro_ms, attn_ms = time_launches(kprologue, attention)
+    # The two-call path, for comparison.
+    ms_per_step_unfused = time_steps(step_unfused)
+    pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
 
     flops_layer = [attn_flops(w.B, w.H, w.T, w.d, W) for W in windows]
     step_flops = sum(flops_layer)
@@ -254,7 +283,8 @@ def main() -> int:
     attn_total_ms = sum(attn_ms)
     achieved = step_flops / (attn_total_ms * 1e-3) / 1e12
     attn_bytes = attn_compulsory_bytes(w.B, w.H, w.T, w.d)
-    pro_bytes = prologue_bytes(w.B, w.H, w.T, w.d)
+    kpro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=1)
+    pro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=2)
     traffic = measured_traffic()
 
     result = {
@@ -272,13 +302,15 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "layers": L,
-            "windows": windows, "step": "per layer: qknorm_rope + attn_fwd",
+            "windows": windows,
+            "step": "per layer: attn_fwd_qknorm (k-only qknorm_rope kernel + attention kernel "
+                    "with in-kernel q norm and rotation)",
             "flops_per_step": step_flops,
         },
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_stream<64, mode>",
+            "kernel": "attn_fwd_bf16_stream<64, mode, qkn=true>",
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -290,11 +322,20 @@ def main() -> int:
             "compulsory_bytes_per_launch": attn_bytes,
             "compulsory_hbm_gbs": round(attn_bytes * L / (attn_total_ms * 1e-3) / 1e9, 1),
         },
-        "prologue": {
-            "avg_launch_us": round(1e3 * sum(pro_ms) / L, 3),
-            "bytes_per_launch": pro_bytes,
-            "achieved_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
+        "k_prologue": {
+            "avg_launch_us": round(1e3 * sum(kpro_ms) / L, 3),
+            "bytes_per_launch": kpro_bytes,
+            "achieved_gbs": round(kpro_bytes * L / (sum(kpro_ms) * 1e-3) / 1e9, 1),
             "peak_gbs": PEAK_HBM_GBS,
+        },
+        "two_call_path": {
+            "ms_per_step": round(ms_per_step_unfused, 5),
+            "value": round(step_flops / (ms_per_step_unfused * 1e-3) / 1e12, 3),
+            "attn_avg_launch_us": round(1e3 * sum(attn_unf_ms) / L, 3),
+            "attn_tflops": round(step_flops / (sum(attn_unf_ms) * 1e-3) / 1e12, 3),
+            "prologue_avg_launch_us": round(1e3 * sum(pro_ms) / L, 3),
+            "prologue_bytes_per_launch": pro_bytes,
+            "prologue_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
         },
     }
     if not args.no_cpu_baseline:

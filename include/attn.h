@@ -14,8 +14,9 @@
  *   - Tensors are dense, contiguous, row-major [B][H][T][d] (batch, head, token, channel).
  *   - Pointers named as device pointers must point to device memory of the current HIP device;
  *     the caller allocates and frees all of them. The library allocates no memory, keeps no
- *     mutable global state, never synchronises the host, and is safe to call from several
- *     threads (the calls are ordered only by the stream the caller passes).
+ *     mutable global state beyond a per-device cache of how many workgroups the GPU holds at
+ *     once, never synchronises the host, and is safe to call from several threads (the calls
+ *     are ordered only by the stream the caller passes).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream. Work is only
  *     enqueued: results are ready once that stream has been synchronised.
  *   - Every entry point validates its arguments before making any HIP call and returns one of the
@@ -91,6 +92,7 @@ int attn_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base, v
  *   q, k            DEVICE [B][H][T][d] of dtype, read
  *   q_out, k_out    DEVICE [B][H][T][d] of dtype, written; q_out may equal q and k_out may equal
  *                   k (in place); any other overlap is ATTN_ERR_ALIAS
+ *   q and q_out may both be NULL: then only k is processed (one of them NULL is ATTN_ERR_NULL)
  *   cos_tab, sin_tab DEVICE fp32 [T][d/2] from attn_rope_table (only rows t < T are read)
  *   d in {16, 32, 64, 128}; eps >= 0 and finite
  */
@@ -120,6 +122,52 @@ int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int T, int d, int window, int causal, int dtype, void* stream);
+
+/*
+ * Attention forward whose kernel applies QK-norm and RoPE to q itself as it loads each block of
+ * q rows (the normalised q is never written to memory); k must already be normalised and
+ * rotated (attn_qknorm_rope with q = NULL, or the k_work of attn_fwd_qknorm), e.g. a layer's
+ * cached keys. Result: attn_fwd(RoPE(RMSNorm(q)), k, v) with lse and out as in attn_fwd.
+ * The softmax runs without a running maximum: a normalised, rotated q row has Euclidean norm
+ * <= sqrt(d), so every score q.k/sqrt(d) lies within |k_j| of 0, and exp of it stays far inside
+ * the fp32 and bf16 ranges for every row of k with Euclidean norm <= 2 sqrt(d) (normalised rows
+ * have norm <= sqrt(d)). Rows of k beyond that bound are outside this entry point's contract.
+ *   q                DEVICE [B][H][T][d] bf16, read (before norm and rotation)
+ *   k                DEVICE [B][H][T][d] bf16, read (after norm and rotation)
+ *   v, out, lse      as in attn_fwd; out must not overlap q, k or v
+ *   cos_tab, sin_tab DEVICE fp32 [T][d/2] from attn_rope_table
+ *   eps              >= 0 and finite, as in attn_qknorm_rope
+ *   window, causal   as in attn_fwd
+ *   d in {32, 64, 128}; dtype must be ATTN_BF16 (else ATTN_ERR_DTYPE)
+ * Rounding differs from attn_qknorm_rope + attn_fwd in one place: q's normalised, rotated row is
+ * multiplied by log2(e)/sqrt(d) in fp32 before its one rounding to bf16.
+ */
+int attn_fwd_qnorm(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const float* cos_tab, const float* sin_tab, int B, int H, int T, int d,
+                   float eps, int window, int causal, int dtype, void* stream);
+
+/*
+ * One attention layer of [HABR] `CausalSelfAttention.forward` after the projections: QK-norm
+ * and RoPE on q and k, then attention, i.e. the result of attn_qknorm_rope followed by attn_fwd.
+ * It runs as attn_qknorm_rope(NULL, k, NULL, k_work, ...) followed by
+ * attn_fwd_qnorm(q, k_work, v, ...): the normalised q is never written to memory. Both
+ * normalised rows have Euclidean norm <= sqrt(d), so every score q.k/sqrt(d) lies in
+ * [-sqrt(d), sqrt(d)] and the softmax runs without a running maximum or rescaling.
+ *   q, k, v          DEVICE [B][H][T][d] bf16, read (q and k before norm and rotation)
+ *   k_work           DEVICE [B][H][T][d] bf16, written with RoPE(RMSNorm(k)) (the caller may
+ *                    keep it, e.g. as the layer's keys); may equal k (normalised in place);
+ *                    any other overlap with q, k, v, out or lse is ATTN_ERR_ALIAS
+ *   out, lse         as in attn_fwd; out must not overlap q, k, v or k_work
+ *   cos_tab, sin_tab DEVICE fp32 [T][d/2] from attn_rope_table
+ *   eps              >= 0 and finite, as in attn_qknorm_rope
+ *   window, causal   as in attn_fwd
+ *   d in {32, 64, 128}; dtype must be ATTN_BF16 (else ATTN_ERR_DTYPE)
+ * Rounding differs from attn_qknorm_rope + attn_fwd in one place: q's normalised, rotated row is
+ * multiplied by log2(e)/sqrt(d) in fp32 before its one rounding to bf16.
+ */
+int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, void* out,
+                    float* lse, const float* cos_tab, const float* sin_tab, int B, int H, int T,
+                    int d, float eps, int window, int causal, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,8 +27,8 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    assert {"attn_fwd", "attn_qknorm_rope", "attn_rope_table", "attn_strerror",
-            "attn_sssl_windows", "attn_version"} <= set(names)
+    assert {"attn_fwd", "attn_fwd_qnorm", "attn_fwd_qknorm", "attn_qknorm_rope",
+            "attn_rope_table", "attn_strerror", "attn_sssl_windows", "attn_version"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -82,7 +82,7 @@ no_gpu = pytest.mark.skipif(
     reason="fake-pointer validation cases only run where no GPU is present")
 
 P = 1 << 20  # 16-byte aligned fake addresses, far apart
-A, Bp, Cp, Dp, Ep, Fp = (P * i for i in range(1, 7))
+A, Bp, Cp, Dp, Ep, Fp, Gp, Hp = (P * i for i in range(1, 9))
 
 
 def fwd_args(**kw):
@@ -145,6 +145,10 @@ QKN_CASES = [
     ("q_out overlaps q", dict(qo=A + 16), _lib.ATTN_ERR_ALIAS),
     ("q_out is k", dict(qo=Bp), _lib.ATTN_ERR_ALIAS),
     ("k_out is q_out", dict(ko=Cp), _lib.ATTN_ERR_ALIAS),
+    ("q null, q_out given", dict(q=None), _lib.ATTN_ERR_NULL),
+    ("q given, q_out null", dict(qo=None), _lib.ATTN_ERR_NULL),
+    ("k only, misaligned k_out", dict(q=None, qo=None, ko=Dp + 8), _lib.ATTN_ERR_ALIGN),
+    ("k only, k_out overlaps k", dict(q=None, qo=None, ko=Bp + 32), _lib.ATTN_ERR_ALIAS),
 ]
 
 
@@ -175,4 +179,78 @@ def test_rope_table_rejects_before_any_hip_call(lib, name, kw, code):
     a = dict(cos=A, sin=Bp, T=64, d=64, base=10000.0, stream=None)
     a.update(kw)
     rc = lib.attn_rope_table(a["cos"], a["sin"], a["T"], a["d"], a["base"], a["stream"])
+    assert rc == code, (name, rc, lib.attn_strerror(rc))
+
+
+def fused_args(**kw):
+    a = dict(q=A, k=Bp, v=Cp, kw=Dp, out=Ep, lse=Fp, cos=Gp, sin=Hp, B=1, H=2, T=64, d=64,
+             eps=1e-6, window=-1, causal=1, dtype=_lib.ATTN_BF16, stream=None)
+    a.update(kw)
+    return a
+
+
+FUSED_CASES = [
+    ("null q", dict(q=None), _lib.ATTN_ERR_NULL),
+    ("null k_work", dict(kw=None), _lib.ATTN_ERR_NULL),
+    ("null cos", dict(cos=None), _lib.ATTN_ERR_NULL),
+    ("f32", dict(dtype=_lib.ATTN_F32), _lib.ATTN_ERR_DTYPE),
+    ("dtype 3", dict(dtype=3), _lib.ATTN_ERR_DTYPE),
+    ("d=16", dict(d=16), _lib.ATTN_ERR_HEAD_DIM),
+    ("d=96", dict(d=96), _lib.ATTN_ERR_HEAD_DIM),
+    ("B=0", dict(B=0), _lib.ATTN_ERR_SHAPE),
+    ("T=-5", dict(T=-5), _lib.ATTN_ERR_SHAPE),
+    ("causal 3", dict(causal=3), _lib.ATTN_ERR_WINDOW),
+    ("noncausal window", dict(causal=0, window=0), _lib.ATTN_ERR_WINDOW),
+    ("eps < 0", dict(eps=-1e-3), _lib.ATTN_ERR_ARG),
+    ("eps inf", dict(eps=float("inf")), _lib.ATTN_ERR_ARG),
+    ("misaligned v", dict(v=Cp + 8), _lib.ATTN_ERR_ALIGN),
+    ("misaligned k_work", dict(kw=Dp + 2), _lib.ATTN_ERR_ALIGN),
+    ("misaligned sin", dict(sin=Hp + 4), _lib.ATTN_ERR_ALIGN),
+    ("misaligned lse", dict(lse=Fp + 1), _lib.ATTN_ERR_ALIGN),
+    ("k_work inside k", dict(kw=Bp + 128), _lib.ATTN_ERR_ALIAS),
+    ("k_work is q", dict(kw=A), _lib.ATTN_ERR_ALIAS),
+    ("k_work is v", dict(kw=Cp), _lib.ATTN_ERR_ALIAS),
+    ("out is k_work", dict(out=Dp), _lib.ATTN_ERR_ALIAS),
+    ("out is k", dict(out=Bp), _lib.ATTN_ERR_ALIAS),
+    ("lse inside k_work", dict(lse=Dp + 64), _lib.ATTN_ERR_ALIAS),
+    ("lse inside out", dict(lse=Ep + 64), _lib.ATTN_ERR_ALIAS),
+    ("grid too large", dict(B=1 << 15, H=1 << 15, T=1 << 10, d=32), _lib.ATTN_ERR_SHAPE),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_attn_fwd_qknorm_rejects_before_any_hip_call(lib, name, kw, code):
+    a = fused_args(**kw)
+    rc = lib.attn_fwd_qknorm(a["q"], a["k"], a["v"], a["kw"], a["out"], a["lse"], a["cos"],
+                             a["sin"], a["B"], a["H"], a["T"], a["d"], a["eps"], a["window"],
+                             a["causal"], a["dtype"], a["stream"])
+    assert rc == code, (name, rc, lib.attn_strerror(rc))
+
+
+QNORM_CASES = [
+    ("null k", dict(k=None), _lib.ATTN_ERR_NULL),
+    ("null sin", dict(sin=None), _lib.ATTN_ERR_NULL),
+    ("f32", dict(dtype=_lib.ATTN_F32), _lib.ATTN_ERR_DTYPE),
+    ("d=16", dict(d=16), _lib.ATTN_ERR_HEAD_DIM),
+    ("H=0", dict(H=0), _lib.ATTN_ERR_SHAPE),
+    ("window -3", dict(window=-3), _lib.ATTN_ERR_WINDOW),
+    ("eps nan", dict(eps=float("nan")), _lib.ATTN_ERR_ARG),
+    ("misaligned q", dict(q=A + 4), _lib.ATTN_ERR_ALIGN),
+    ("misaligned cos", dict(cos=Gp + 8), _lib.ATTN_ERR_ALIGN),
+    ("out is q", dict(out=A), _lib.ATTN_ERR_ALIAS),
+    ("out inside v", dict(out=Cp + 4096), _lib.ATTN_ERR_ALIAS),
+    ("lse inside q", dict(lse=A + 16), _lib.ATTN_ERR_ALIAS),
+    ("slab too large", dict(B=1, H=1, T=1 << 23, d=128, **{n: (i + 1) << 40 for i, n in enumerate(
+        ("q", "k", "v", "out", "lse", "cos", "sin"))}), _lib.ATTN_ERR_SHAPE),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", QNORM_CASES, ids=[c[0] for c in QNORM_CASES])
+def test_attn_fwd_qnorm_rejects_before_any_hip_call(lib, name, kw, code):
+    a = fused_args(**kw)
+    rc = lib.attn_fwd_qnorm(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cos"], a["sin"],
+                            a["B"], a["H"], a["T"], a["d"], a["eps"], a["window"], a["causal"],
+                            a["dtype"], a["stream"])
     assert rc == code, (name, rc, lib.attn_strerror(rc))

@@ -31,3 +31,9 @@ def test_bench_refuses_more_than_one_gpu(capsys, monkeypatch):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_prologue_bytes():
+    # each tensor read once and written once, bf16
+    assert bench.prologue_bytes(16, 12, 1024, 64, tensors=1) == 16 * 12 * 1024 * 64 * 2 * 2
+    assert bench.prologue_bytes(16, 12, 1024, 64) == 2 * bench.prologue_bytes(16, 12, 1024, 64, tensors=1)

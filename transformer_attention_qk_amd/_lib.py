@@ -26,6 +26,12 @@ SIGNATURES = {
                                  c_int, c_int, c_int, c_int, c_float, c_int, c_void_p]),
     "attn_fwd": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                          c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p]),
+    "attn_fwd_qnorm": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_int, c_int, c_int, c_int, c_float, c_int, c_int,
+                               c_int, c_void_p]),
+    "attn_fwd_qknorm": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_float,
+                                c_int, c_int, c_int, c_void_p]),
 }
 
 # status codes (include/attn.h)

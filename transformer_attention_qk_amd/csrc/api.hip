@@ -91,21 +91,25 @@ int attn_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base, v
 int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos_tab,
                      const float* sin_tab, int B, int H, int T, int d, float eps, int dtype,
                      void* stream) {
-  if (!q || !k || !q_out || !k_out || !cos_tab || !sin_tab) return ATTN_ERR_NULL;
+  // q and q_out are both given or both NULL (then only k is processed).
+  if (!k || !k_out || !cos_tab || !sin_tab || (q == nullptr) != (q_out == nullptr))
+    return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   int64_t n = 0;
   if (int rc = check_shape(B, H, T, d, &n)) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ATTN_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
+  if ((q && !aligned16(q)) || !aligned16(k) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
       !aligned16(cos_tab) || !aligned16(sin_tab))
     return ATTN_ERR_ALIGN;
   const int64_t bytes = n * elem_bytes(dtype);
-  if (q_out != q && overlap(q_out, bytes, q, bytes)) return ATTN_ERR_ALIAS;
   if (k_out != k && overlap(k_out, bytes, k, bytes)) return ATTN_ERR_ALIAS;
-  if (overlap(q_out, bytes, k, bytes) || overlap(k_out, bytes, q, bytes) ||
-      overlap(q_out, bytes, k_out, bytes))
-    return ATTN_ERR_ALIAS;
+  if (q != nullptr) {
+    if (q_out != q && overlap(q_out, bytes, q, bytes)) return ATTN_ERR_ALIAS;
+    if (overlap(q_out, bytes, k, bytes) || overlap(k_out, bytes, q, bytes) ||
+        overlap(q_out, bytes, k_out, bytes))
+      return ATTN_ERR_ALIAS;
+  }
   hipError_t e = attn::launch_qknorm_rope(q, k, q_out, k_out, cos_tab, sin_tab, B, H, T, d, eps,
                                           dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -146,6 +150,80 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   else
     e = attn::launch_attn_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)out,
                                   lse, B, H, T, d, window, causal, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+namespace {
+
+// Checks shared by attn_fwd_qnorm and attn_fwd_qknorm (k here is the tensor the attention
+// kernel reads as keys).
+int check_qnorm_args(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
+                     int T, int d, float eps, int window, int causal, int dtype, int64_t* n) {
+  if (!q || !k || !v || !out || !cos_tab || !sin_tab) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (int rc = check_shape(B, H, T, d, n)) return rc;
+  if (causal != 0 && causal != 1) return ATTN_ERR_WINDOW;
+  if (window < -1 || (causal == 0 && window != -1)) return ATTN_ERR_WINDOW;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return ATTN_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(cos_tab) ||
+      !aligned16(sin_tab))
+    return ATTN_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
+  const int64_t bytes = *n * 2;
+  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) ||
+      overlap(out, bytes, v, bytes))
+    return ATTN_ERR_ALIAS;
+  const int64_t bh = (int64_t)B * H;
+  if (lse != nullptr) {
+    const int64_t lbytes = bh * T * 4;
+    if (overlap(lse, lbytes, q, bytes) || overlap(lse, lbytes, k, bytes) ||
+        overlap(lse, lbytes, v, bytes) || overlap(lse, lbytes, out, bytes))
+      return ATTN_ERR_ALIAS;
+  }
+  // 32-bit buffer offsets: one head's slab plus a query block, and the rotation tables.
+  if (((int64_t)T + 128) * d * 2 >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
+  if (bh * ((T + 127) / 128) > kMaxGrid) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+int attn_fwd_qnorm(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const float* cos_tab, const float* sin_tab, int B, int H, int T, int d,
+                   float eps, int window, int causal, int dtype, void* stream) {
+  int64_t n = 0;
+  if (int rc = check_qnorm_args(q, k, v, out, lse, cos_tab, sin_tab, B, H, T, d, eps, window,
+                                causal, dtype, &n))
+    return rc;
+  const hipError_t e = attn::launch_attn_fwd_bf16_qknorm(q, k, v, out, lse, cos_tab, sin_tab, eps,
+                                                         B, H, T, d, window, causal,
+                                                         (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, void* out,
+                    float* lse, const float* cos_tab, const float* sin_tab, int B, int H, int T,
+                    int d, float eps, int window, int causal, int dtype, void* stream) {
+  if (!k_work) return ATTN_ERR_NULL;
+  int64_t n = 0;
+  if (int rc = check_qnorm_args(q, k_work, v, out, lse, cos_tab, sin_tab, B, H, T, d, eps,
+                                window, causal, dtype, &n))
+    return rc;
+  if (!k) return ATTN_ERR_NULL;
+  if (!aligned16(k)) return ATTN_ERR_ALIGN;
+  const int64_t bytes = n * 2;
+  if (k_work != k && overlap(k_work, bytes, k, bytes)) return ATTN_ERR_ALIAS;
+  if (overlap(k_work, bytes, q, bytes) || overlap(k_work, bytes, v, bytes) ||
+      overlap(out, bytes, k, bytes))
+    return ATTN_ERR_ALIAS;
+  if (lse != nullptr && overlap(lse, (int64_t)B * H * T * 4, k, bytes)) return ATTN_ERR_ALIAS;
+  hipError_t e = attn::launch_qknorm_rope(nullptr, k, nullptr, k_work, cos_tab, sin_tab, B, H, T,
+                                          d, eps, ATTN_BF16, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = attn::launch_attn_fwd_bf16_qknorm(q, k_work, v, out, lse, cos_tab, sin_tab, eps, B, H, T,
+                                          d, window, causal, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

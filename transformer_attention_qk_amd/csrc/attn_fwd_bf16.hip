@@ -175,7 +175,15 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Per-wave state and stages of one item (block of 128 queries of one head).
-template <int D, int MODE>
+//
+// QKN = true: the Q rows arrive raw and are RMS-normalised, rotated and scaled by log2(e)/sqrt(d)
+// here (fp32, one rounding to bf16), and K rows arrive normalised and rotated. Each such row has
+// Euclidean norm at most sqrt(d), so a score q.k/sqrt(d) lies in [-sqrt(d), sqrt(d)] and
+// exp2 of a score in base-2 units lies in [2^-(sqrt(d) log2 e), 2^(sqrt(d) log2 e)]
+// (2^-16.4 .. 2^16.4 at d = 128): the softmax needs no running maximum, no rescaling and no
+// subtraction, and its weights and sums stay far inside the bf16 and fp32 ranges. The row sum of
+// T such weights stays finite for any T below 2^100.
+template <int D, int MODE, bool QKN>
 struct WaveTile {
   using C = FwdCfg<D>;
   static constexpr bool causal = MODE != kNonCausal;
@@ -224,7 +232,7 @@ struct WaveTile {
     }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-    m_run = -INFINITY;
+    m_run = QKN ? 0.f : -INFINITY;
     l_run0 = 0.f;
     l_run1 = 0.f;
   }
@@ -244,18 +252,108 @@ struct WaveTile {
     return (t * C::BN >= f_lo) & (t * C::BN + 2 * C::BN <= f_hi);
   }
 
-  __device__ __forceinline__ void q_from_global(__amdgpu_buffer_rsrc_t rq) {
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(qi * C::ROW_BYTES + 32 * s + 16 * hi)));
+  // Rotation factors of the lane's Q row at the frequencies it holds (QKN only): cos and sin at
+  // columns 16 s + 8 hi .. +8 for s < KSTEPS/2, as 16-byte loads.
+  struct Rope {
+    f32x4 c[C::KSTEPS / 2][2], s[C::KSTEPS / 2][2];
+  };
+  // The lane index, recomputed where it is used (the item transitions) instead of keeping the
+  // values derived from it live through the tile loop.
+  __device__ __forceinline__ int lane_now() const {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
   }
-  // Q block staged in LDS with the K layout: wave w reads rows 32 w + l32 (the swizzle of those
-  // rows equals that of l32).
-  __device__ __forceinline__ void q_from_lds(const char* qbuf) {
-    const char* qb = qbuf + 32 * wave * C::ROW_BYTES + k_row_off;
+  __device__ __forceinline__ int q_row(int q0) const { return q0 + 32 * wave + (lane_now() & 31); }
+  __device__ __forceinline__ void load_rope(int q0, const float* cos_tab, const float* sin_tab,
+                                            Rope& r) const {
+    if constexpr (QKN) {
+      // Buffer loads with one 32-bit offset register: the tables' T * d/2 floats are far below
+      // 2^31 bytes (T * d < 2^30 is checked before launch).
+      constexpr int HALF = D / 2;
+      const int tab_bytes = T * HALF * 4;
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(cos_tab), (short)0, tab_bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(sin_tab), (short)0, tab_bytes, kBufferWord3);
+      const uint32_t off = (uint32_t)(min(q_row(q0), T - 1) * HALF + 8 * (lane_now() >> 5)) * 4;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS / 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          r.c[s][h] = __builtin_bit_cast(f32x4, buffer_load16(rc, off + 64 * s + 16 * h));
+          r.s[s][h] = __builtin_bit_cast(f32x4, buffer_load16(rs, off + 64 * s + 16 * h));
+        }
+    }
+  }
+  // This lane's raw Q values xf[s] = Q[row][16 s + 8 hi .. +8) of the item at q0, from global
+  // memory (rows past T read as zero) or from the Q block staged in LDS with the K layout (wave
+  // w reads rows 32 w + l32, whose swizzle equals that of l32).
+  __device__ __forceinline__ void load_q_global(__amdgpu_buffer_rsrc_t rq, int q0,
+                                                bf16x8 (&xf)[C::KSTEPS]) const {
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(qb + 16 * ((2 * s + hi) ^ k_swz));
+      xf[s] = __builtin_bit_cast(
+          bf16x8, buffer_load16(rq, (uint32_t)(q_row(q0) * C::ROW_BYTES + 32 * s + 16 * hi)));
+  }
+  __device__ __forceinline__ void load_q_lds(const char* qbuf, bf16x8 (&xf)[C::KSTEPS]) const {
+    const int ln = lane_now();
+    const int r = ln & 31, h = ln >> 5, sw = swz_k<D>(r);
+    const char* qb = qbuf + (32 * wave + r) * C::ROW_BYTES;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+      xf[s] = *reinterpret_cast<const bf16x8*>(qb + 16 * ((2 * s + h) ^ sw));
+  }
+  // qf (the Q^T fragments, B operand of the scores) of the item at q0 from the raw values. With
+  // QKN the row is normalised (weightless RMSNorm over the head dim; the other half of the row
+  // sits in lane l ^ 32), rotated by the half-split rotation at its position (column j < d/2
+  // pairs with column j + d/2, which is in xf[s + KSTEPS/2] of the same lane) and scaled by
+  // log2(e)/sqrt(d), in fp32; rows past T become zero.
+  __device__ __forceinline__ void set_q(const bf16x8 (&xf)[C::KSTEPS], const Rope& rope, int q0,
+                                        float eps) {
+    if constexpr (!QKN) {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) qf[s] = xf[s];
+    } else {
+      float x[C::KSTEPS][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        const u32x4 w = __builtin_bit_cast(u32x4, xf[s]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[s][2 * e] = bf16lo_to_f32(w[e]);
+          x[s][2 * e + 1] = bf16hi_to_f32(w[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[s][e], x[s][e], ss);
+      }
+      ss = pair_sum(ss);
+      const float rinv = (q_row(q0) < T)
+                             ? (kLog2e * (1.0f / sqrtf((float)D))) / sqrtf(ss * (1.0f / D) + eps)
+                             : 0.f;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS / 2; ++s) {
+        u32x4 w1, w2;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float c = rope.c[s][(e + u) >> 2][(e + u) & 3];
+            const float sn = rope.s[s][(e + u) >> 2][(e + u) & 3];
+            const float a = x[s][e + u] * rinv;
+            const float b = x[s + C::KSTEPS / 2][e + u] * rinv;
+            y1[u] = fmaf(a, c, b * sn);
+            y2[u] = fmaf(b, c, -(a * sn));
+          }
+          w1[e / 2] = pack_bf16x2(y1[0], y1[1]);
+          w2[e / 2] = pack_bf16x2(y2[0], y2[1]);
+        }
+        qf[s] = __builtin_bit_cast(bf16x8, w1);
+        qf[s + C::KSTEPS / 2] = __builtin_bit_cast(bf16x8, w2);
+      }
+    }
   }
 
   // Scores of tile t (K tile at kbuf) for the blocks this wave sees. INTERLEAVE runs the two
@@ -287,7 +385,8 @@ struct WaveTile {
     }
   }
 
-  // Mask the scores of tile t and return their row maximum (raw, pair-reduced).
+  // Mask the scores of tile t and return their row maximum (raw, pair-reduced; with QKN only the
+  // mask is applied and 0 is returned).
   template <bool FAST>
   __device__ __forceinline__ float mask_max(int t, f32x16 (&sa)[2]) {
 #pragma unroll
@@ -300,23 +399,28 @@ struct WaveTile {
         }
         if (!full(t, kb)) {
           // Register r holds key b0 + c_r with c_r = 8 (r / 4) + r % 4. With dq = qi - b0, the
-          // key is visible iff 0 <= dq - c_r (causal) and dq - c_r <= window (one unsigned
-          // compare covers both), and b0 + c_r < T where the block runs past the sequence end.
+          // key is visible iff c_r <= dq (causal), c_r >= dq - window (window) and
+          // c_r <= T - 1 - b0 (sequence end): one upper limit per lane, so each register needs
+          // one compare (two with a window) whose result is used at once.
           const int b0 = t * C::BN + 32 * kb + 4 * hi;
           const int dq = qi - b0;
-          const bool tail = t * C::BN + 32 * kb + 32 > T;  // wave-uniform
+          int hi_c = causal ? dq : 0x7fffffff;
+          if (t * C::BN + 32 * kb + 32 > T) hi_c = min(hi_c, T - 1 - b0);  // wave-uniform test
+          int lo_c = dq - window;
+          // Opaque to the optimiser: otherwise it hoists the 16-32 per-register lane masks of a
+          // loop-invariant edge out of the loops and spills them.
+          asm volatile("" : "+v"(hi_c), "+v"(lo_c));
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
-            bool vis = true;
-            if constexpr (MODE == kCausal) vis = dq >= c;
-            if constexpr (MODE == kCausalWindow) vis = (unsigned)(dq - c) <= (unsigned)window;
-            if (tail) vis = vis & (b0 + c < T);
+            bool vis = c <= hi_c;
+            if constexpr (MODE == kCausalWindow) vis = vis & (c >= lo_c);
             sa[kb][r] = vis ? sa[kb][r] : -INFINITY;
           }
         }
       }
     }
+    if constexpr (QKN) return 0.f;
     // Tree reduction over the 32 values of the lane, then across the lane pair.
     float m8[8];
 #pragma unroll
@@ -328,8 +432,9 @@ struct WaveTile {
     return pair_max(fmaxf(m2a, m2b));
   }
 
-  // Lazy running-maximum update with a tile's row maximum (raw scores).
+  // Lazy running-maximum update with a tile's row maximum (raw scores); nothing with QKN.
   __device__ __forceinline__ void decide(float mx) {
+    if constexpr (QKN) return;
     const float m_tile = mx * scale_log2;
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
@@ -344,8 +449,9 @@ struct WaveTile {
     }
   }
 
-  // P = exp2(s * scale - m), rounded to bf16 in the B-operand order of the P V product; the row
-  // sums add the rounded values.
+  // P = exp2(s * scale - m) (with QKN: exp2(s), the scores being in base-2 units already),
+  // rounded to bf16 in the B-operand order of the P V product; the row sums add the rounded
+  // values.
   __device__ __forceinline__ void exps(const f32x16 (&sa)[2], bf16x8 (&pf)[2][2]) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
@@ -355,8 +461,14 @@ struct WaveTile {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[kb][8 * tt + 2 * e], scale_log2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[kb][8 * tt + 2 * e + 1], scale_log2, -m_use));
+          float p0, p1;
+          if constexpr (QKN) {
+            p0 = __builtin_amdgcn_exp2f(sa[kb][8 * tt + 2 * e]);
+            p1 = __builtin_amdgcn_exp2f(sa[kb][8 * tt + 2 * e + 1]);
+          } else {
+            p0 = __builtin_amdgcn_exp2f(fmaf(sa[kb][8 * tt + 2 * e], scale_log2, -m_use));
+            p1 = __builtin_amdgcn_exp2f(fmaf(sa[kb][8 * tt + 2 * e + 1], scale_log2, -m_use));
+          }
           w[e] = pack_bf16x2(p0, p1);
           if (e & 1)
             l_run1 = add_bf16_pair(w[e], l_run1);
@@ -442,16 +554,17 @@ __device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, i
 // ---------------------------------------------------------------------------------------------
 // Streaming kernel (d <= 64): persistent grid, direct-to-LDS K/V stream, pipelined tiles.
 // ---------------------------------------------------------------------------------------------
-template <int D, int MODE>
+template <int D, int MODE, bool QKN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int window_arg,
+    bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
+    const float* __restrict__ sin_tab, float eps, int BH, int T, int window_arg,
     float scale_log2, int nqt) {
   using C = FwdCfg<D>;
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::STREAM_LDS];
   const int tid = threadIdx.x;
-  WaveTile<D, MODE> w;
+  WaveTile<D, MODE, QKN> w;
   w.init(T, window, scale_log2, tid);
   const int P = (int)gridDim.x;
   const int g = (int)blockIdx.x;
@@ -533,8 +646,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   w.set_item(q0);
   issue_next();
   issue_next();
-  w.q_from_global(head_rsrc(Q + (int64_t)bh * T * D, slab));
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  typename WaveTile<D, MODE, QKN>::Rope rope;
+  {
+    bf16x8 xf[C::KSTEPS];
+    w.load_q_global(head_rsrc(Q + (int64_t)bh * T * D, slab), q0, xf);
+    w.load_rope(q0, cos_tab, sin_tab, rope);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    w.set_q(xf, rope, q0, eps);
+  }
   __syncthreads();
   issue_next();
   unsigned st_comp = 0;  // stage of the tile being consumed
@@ -564,15 +683,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     // alongside the mask and maximum of t+1; running-maximum update; wait until the stream tile
     // two ahead has landed; barrier. The item's last tile also fetches the next item's Q block,
     // issued before the stream tile so the same wait covers it.
-    auto body = [&](int t, f32x16(&cur)[2], f32x16(&nxt)[2]) {
-      const bool has_next = t + 1 < te;
+    // HAS_NEXT: t + 1 < te, fixed at compile time so that the last tile of an item has its own
+    // code, where the registers of the rotation factors are free.
+    auto body = [&](auto has_next_c, int t, f32x16(&cur)[2], f32x16(&nxt)[2]) {
+      constexpr bool has_next = decltype(has_next_c)::value;
       if (!has_next && more) dma_q(nbh, nq0);
       issue_next();
       const char* kn = smem + ((st_comp + 1) & (C::NSTAGE - 1)) * (2 * C::TILE_BYTES);
       const char* vc = smem + st_comp * (2 * C::TILE_BYTES) + C::TILE_BYTES;
       bf16x8 pf[2][2];
       float mx = -INFINITY;
-      if (w.fast2(t)) {
+      if (has_next && w.fast2(t)) {
         w.template scores<true, true>(kn, t + 1, nxt);
         w.exps(cur, pf);
         w.template pv<true>(vc, t, pf);
@@ -583,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
 #pragma unroll
         for (int j = 0; j < 2 * C::KSTEPS; ++j) {
           __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 96 / (2 * C::KSTEPS), 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, (QKN ? 64 : 96) / (2 * C::KSTEPS), 0);
         }
         // Phase B: the P V MFMAs of t, each with its V reads issued two MFMAs ahead, alternate
         // with the mask and maximum of t+1.
@@ -592,44 +713,68 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
         for (int j = 0; j < 4 * C::DB; ++j) {
           __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
           if (j + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
+          if constexpr (!QKN) __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
         }
-      } else {
-        if (has_next) w.template scores<false, true>(kn, t + 1, nxt);
+      } else if constexpr (has_next) {
+        w.template scores<false, true>(kn, t + 1, nxt);
         if (w.any(t)) {
           w.exps(cur, pf);
           w.template pv<false>(vc, t, pf);
         }
-        if (has_next) mx = w.template mask_max<false>(t + 1, nxt);
+        mx = w.template mask_max<false>(t + 1, nxt);
+      } else {
+        if (w.any(t)) {
+          w.exps(cur, pf);
+          w.template pv<false>(vc, t, pf);
+        }
       }
       if (has_next) w.decide(mx);
       wait_vmcnt<(C::PREFETCH - 2) * C::DMA_PER_TILE>();  // the tile two stages ahead has landed
       __syncthreads();
       st_comp = (st_comp + 1) & (C::NSTAGE - 1);
     };
+    const std::true_type more_tiles;
+    const std::false_type last_tile;
     int t = tb;
-    for (; t + 1 < te; t += 2) {
-      body(t, sacc[0], sacc[1]);
-      body(t + 1, sacc[1], sacc[0]);
+    for (; t + 2 < te; t += 2) {
+      body(more_tiles, t, sacc[0], sacc[1]);
+      body(more_tiles, t + 1, sacc[1], sacc[0]);
     }
-    if (t < te) body(t, sacc[0], sacc[1]);
+    if (t + 1 < te) {
+      body(more_tiles, t, sacc[0], sacc[1]);
+      sacc[0][0] = sacc[1][0];
+      sacc[0][1] = sacc[1][1];
+      ++t;
+    }
+    // One instance of the last step (two would invite the compiler to hoist their common loads
+    // above the branch, into code where those registers are taken).
+    body(last_tile, t, sacc[0], sacc[1]);
 
     // Item epilogue, after the barrier so the stores do not sit between a stream tile's loads
-    // and the wait for them.
-    w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
+    // and the wait for them. The next item's Q fragments are formed first: no store is then in
+    // flight between the rotation factors' loads and their use.
     if (!more) {
+      w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
       // The stream's last loads (out of range, writing zeros) land before the workgroup's LDS
       // is released.
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       break;
     }
+    {
+      // (QKN) the rotation factors of the new rows are loaded here; held through the item's
+      // last tile step they would push that code past the register budget.
+      w.load_rope(nq0, cos_tab, sin_tab, rope);
+      bf16x8 xf[C::KSTEPS];
+      w.load_q_lds(qbuf, xf);
+      w.set_q(xf, rope, nq0, eps);
+    }
+    w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
     ++k;
     bh = nbh;
     q0 = nq0;
     tb = ntb;
     te = nte;
     w.set_item(q0);
-    w.q_from_lds(qbuf);
     // Every wave has its Q fragments before anyone issues the next Q block into the buffer.
     __syncthreads();
   }
@@ -638,16 +783,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
 // ---------------------------------------------------------------------------------------------
 // Tile kernel (d = 128): one workgroup per item, K/V staged through registers one tile ahead.
 // ---------------------------------------------------------------------------------------------
-template <int D, int MODE>
+template <int D, int MODE, bool QKN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int window_arg,
+    bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
+    const float* __restrict__ sin_tab, float eps, int BH, int T, int window_arg,
     float scale_log2, int nqt) {
   using C = FwdCfg<D>;
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::TILE_LDS];
   const int tid = threadIdx.x;
-  WaveTile<D, MODE> w;
+  WaveTile<D, MODE, QKN> w;
   w.init(T, window, scale_log2, tid);
   const int bh = (int)(blockIdx.x % BH);
   const int q0 = (nqt - 1 - (int)(blockIdx.x / BH)) * C::BM;  // heaviest query block first
@@ -658,7 +804,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
   int tb, te;
   item_tiles<D, MODE>(q0, T, window, tb, te);
   w.set_item(q0);
-  w.q_from_global(head_rsrc(Q + hoff, slab));
+  {
+    bf16x8 xf[C::KSTEPS];
+    typename WaveTile<D, MODE, QKN>::Rope rope;
+    w.load_q_global(head_rsrc(Q + hoff, slab), q0, xf);
+    w.load_rope(q0, cos_tab, sin_tab, rope);
+    w.set_q(xf, rope, q0, eps);
+  }
 
   auto gload = [&](__amdgpu_buffer_rsrc_t r, int t, bool needed, u32x4(&st)[C::LPT]) {
 #pragma unroll
@@ -720,45 +872,73 @@ static hipError_t resident_workgroups(Kern kern, int* out) {
   return hipSuccess;
 }
 
-template <int D, int MODE>
-static hipError_t launch_bf16_t(const void* q, const void* k, const void* v, void* out, float* lse,
-                                int B, int H, int T, int window, hipStream_t stream) {
-  const int BH = B * H;
-  const int nqt = (T + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
+// Launch arguments shared by the entry points.
+struct Bf16Args {
+  const void *q, *k, *v;
+  void* out;
+  float* lse;
+  const float *cos_tab, *sin_tab;
+  float eps;
+  int B, H, T, window;
+};
+
+template <int D, int MODE, bool QKN>
+static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
+  const int BH = a.B * a.H;
+  const int nqt = (a.T + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
   const int64_t n_items = (int64_t)BH * nqt;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   if constexpr (D <= 64) {
     int resident = 0;
-    hipError_t e = resident_workgroups(attn_fwd_bf16_stream<D, MODE>, &resident);
+    hipError_t e = resident_workgroups(attn_fwd_bf16_stream<D, MODE, QKN>, &resident);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
-    hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE>), dim3(grid), dim3(256), 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, BH, T,
-                       window, scale_log2, nqt);
+    hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN>), dim3(grid), dim3(256), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse,
+                       a.cos_tab, a.sin_tab, a.eps, BH, a.T, a.window, scale_log2, nqt);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE>), dim3((unsigned)n_items), dim3(256), 0,
-                       stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)out, lse, BH,
-                       T, window, scale_log2, nqt);
+    hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE, QKN>), dim3((unsigned)n_items), dim3(256), 0,
+                       stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out,
+                       a.lse, a.cos_tab, a.sin_tab, a.eps, BH, a.T, a.window, scale_log2, nqt);
   }
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_bf16_d(const void* q, const void* k, const void* v, void* out, float* lse,
-                                int B, int H, int T, int window, int causal, hipStream_t stream) {
+template <int D, bool QKN>
+static hipError_t launch_bf16_d(Bf16Args a, int causal, hipStream_t stream) {
   // A window of T - 1 or more hides nothing: run it as plain causal.
-  if (!causal) return launch_bf16_t<D, kNonCausal>(q, k, v, out, lse, B, H, T, -1, stream);
-  if (window < 0 || window >= T - 1) return launch_bf16_t<D, kCausal>(q, k, v, out, lse, B, H, T, -1, stream);
-  return launch_bf16_t<D, kCausalWindow>(q, k, v, out, lse, B, H, T, window, stream);
+  if (!causal) {
+    a.window = -1;
+    return launch_bf16_t<D, kNonCausal, QKN>(a, stream);
+  }
+  if (a.window < 0 || a.window >= a.T - 1) {
+    a.window = -1;
+    return launch_bf16_t<D, kCausal, QKN>(a, stream);
+  }
+  return launch_bf16_t<D, kCausalWindow, QKN>(a, stream);
+}
+
+template <bool QKN>
+static hipError_t launch_bf16(const Bf16Args& a, int d, int causal, hipStream_t stream) {
+  if (d == 32) return launch_bf16_d<32, QKN>(a, causal, stream);
+  if (d == 64) return launch_bf16_d<64, QKN>(a, causal, stream);
+  if (d == 128) return launch_bf16_d<128, QKN>(a, causal, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                                 int B, int H, int T, int d, int window, int causal,
                                 hipStream_t stream) {
-  if (d == 32) return launch_bf16_d<32>(q, k, v, out, lse, B, H, T, window, causal, stream);
-  if (d == 64) return launch_bf16_d<64>(q, k, v, out, lse, B, H, T, window, causal, stream);
-  if (d == 128) return launch_bf16_d<128>(q, k, v, out, lse, B, H, T, window, causal, stream);
-  return hipErrorInvalidValue;
+  const Bf16Args a{q, k, v, out, lse, nullptr, nullptr, 0.f, B, H, T, window};
+  return launch_bf16<false>(a, d, causal, stream);
+}
+
+hipError_t launch_attn_fwd_bf16_qknorm(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, const float* cos_tab, const float* sin_tab,
+                                       float eps, int B, int H, int T, int d, int window,
+                                       int causal, hipStream_t stream) {
+  const Bf16Args a{q, k, v, out, lse, cos_tab, sin_tab, eps, B, H, T, window};
+  return launch_bf16<true>(a, d, causal, stream);
 }
 
 }  // namespace attn

@@ -76,11 +76,12 @@ struct Vec<float, 4> {
 template <typename Elem>
 constexpr int kE = (sizeof(Elem) == 2) ? 8 : 4;
 
+// Rows [0, q_rows) are rows of q, rows [q_rows, q_rows + rows) rows of k (q_rows = 0: k only).
 template <typename Elem, int D>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const Elem* __restrict__ q, const Elem* __restrict__ k, Elem* q_out, Elem* k_out,
-    const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, int64_t rows, int T,
-    float eps) {
+    const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, int64_t q_rows,
+    int64_t rows, int T, float eps) {
   constexpr int E = kE<Elem>;
   constexpr int HALF = D / 2;
   static_assert(HALF % E == 0, "half head dim must be a multiple of the lane vector");
@@ -90,9 +91,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   const int sub = threadIdx.x % L;
   // Every lane of a row group shares `row`, so a group is either fully active or fully inactive
   // and the xor shuffles below never read a lane of another row.
-  if (row >= 2 * rows) return;
-  const bool is_q = row < rows;
-  const int64_t r = is_q ? row : row - rows;
+  if (row >= q_rows + rows) return;
+  const bool is_q = row < q_rows;
+  const int64_t r = is_q ? row : row - q_rows;
   const Elem* src = (is_q ? q : k) + r * D;
   Elem* dst = (is_q ? q_out : k_out) + r * D;
   const int t = (int)(r % T);
@@ -135,10 +136,11 @@ static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out
   constexpr int L = (D / 2) / kE<Elem>;
   constexpr int ROWS_PER_BLOCK = 256 / L;
   const int64_t rows = (int64_t)B * H * T;
-  const int64_t grid = (2 * rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  const int64_t q_rows = (q != nullptr) ? rows : 0;
+  const int64_t grid = (q_rows + rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
   hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D>), dim3((unsigned)grid), dim3(256), 0, stream,
                      (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, cos_tab, sin_tab,
-                     rows, T, eps);
+                     q_rows, rows, T, eps);
   return hipGetLastError();
 }
 

@@ -56,26 +56,31 @@ def rope_table(T: int, d: int, base: float = 10000.0, device=None) -> tuple[torc
     return cos, sin
 
 
-def qknorm_rope(q: torch.Tensor, k: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+def qknorm_rope(q: torch.Tensor | None, k: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
                 eps: float = 1e-6, q_out: torch.Tensor | None = None,
-                k_out: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
-    """QK-RMSNorm + RoPE of q, k [B, H, T, d]; outputs may be q, k themselves (in place)."""
+                k_out: torch.Tensor | None = None):
+    """QK-RMSNorm + RoPE of q, k [B, H, T, d]; outputs may be q, k themselves (in place).
+    With q None only k is processed (the returned q_out is None)."""
     lib = _lib.load()
-    _require(q, "q")
-    if q.dim() != 4 or q.dtype not in _DTYPES:
-        raise ValueError("q must be [B, H, T, d] bf16 or fp32")
-    B, H, T, d = q.shape
-    _require(k, "k", q.shape, q.dtype)
+    _require(k, "k")
+    if k.dim() != 4 or k.dtype not in _DTYPES:
+        raise ValueError("k must be [B, H, T, d] bf16 or fp32")
+    B, H, T, d = k.shape
+    if q is not None:
+        _require(q, "q", k.shape, k.dtype)
     _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
     _require(sin, "sin", cos.shape, torch.float32)
     if cos.shape[0] < T:
         raise ValueError("rope tables are shorter than the sequence")
-    q_out = torch.empty_like(q) if q_out is None else q_out
+    if q is not None:
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        _require(q_out, "q_out", k.shape, k.dtype)
+    else:
+        q_out = None
     k_out = torch.empty_like(k) if k_out is None else k_out
-    _require(q_out, "q_out", q.shape, q.dtype)
-    _require(k_out, "k_out", q.shape, q.dtype)
+    _require(k_out, "k_out", k.shape, k.dtype)
     rc = lib.attn_qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin),
-                              B, H, T, d, float(eps), _DTYPES[q.dtype], _stream_handle())
+                              B, H, T, d, float(eps), _DTYPES[k.dtype], _stream_handle())
     _lib.check("attn_qknorm_rope", rc)
     return q_out, k_out
 
@@ -106,10 +111,75 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int = -1
     return out, lse
 
 
+def attn_fwd_qnorm(q: torch.Tensor, kn: torch.Tensor, v: torch.Tensor, cos: torch.Tensor,
+                   sin: torch.Tensor, window: int = -1, causal: bool = True, eps: float = 1e-6,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   want_lse: bool = True):
+    """Attention of raw bf16 q (normalised and rotated inside the kernel) against already
+    normalised and rotated keys kn. Returns (out, lse)."""
+    lib = _lib.load()
+    _require(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    _require(kn, "kn", q.shape, q.dtype)
+    _require(v, "v", q.shape, q.dtype)
+    _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
+    _require(sin, "sin", cos.shape, torch.float32)
+    if cos.shape[0] < T:
+        raise ValueError("rope tables are shorter than the sequence")
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.shape, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", (B, H, T), torch.float32)
+    rc = lib.attn_fwd_qnorm(_ptr(q), _ptr(kn), _ptr(v), _ptr(out), _ptr(lse), _ptr(cos),
+                            _ptr(sin), B, H, T, d, float(eps), int(window), int(bool(causal)),
+                            _lib.ATTN_BF16, _stream_handle())
+    _lib.check("attn_fwd_qnorm", rc)
+    return out, lse
+
+
+def attn_fwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torch.Tensor,
+                    sin: torch.Tensor, window: int = -1, causal: bool = True, eps: float = 1e-6,
+                    k_work: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None, want_lse: bool = True):
+    """QK-norm + RoPE of raw bf16 q, k and attention in one library call.
+
+    Returns (out, lse, k_work); k_work holds RoPE(RMSNorm(k)) (it may be ``k`` itself).
+    """
+    lib = _lib.load()
+    _require(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    _require(k, "k", q.shape, q.dtype)
+    _require(v, "v", q.shape, q.dtype)
+    _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
+    _require(sin, "sin", cos.shape, torch.float32)
+    if cos.shape[0] < T:
+        raise ValueError("rope tables are shorter than the sequence")
+    k_work = torch.empty_like(k) if k_work is None else k_work
+    _require(k_work, "k_work", q.shape, q.dtype)
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.shape, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", (B, H, T), torch.float32)
+    rc = lib.attn_fwd_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(k_work), _ptr(out), _ptr(lse),
+                             _ptr(cos), _ptr(sin), B, H, T, d, float(eps), int(window),
+                             int(bool(causal)), _lib.ATTN_BF16, _stream_handle())
+    _lib.check("attn_fwd_qknorm", rc)
+    return out, lse, k_work
+
+
 def attention_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torch.Tensor,
                     sin: torch.Tensor, window: int = -1, eps: float = 1e-6,
                     qn: torch.Tensor | None = None, kn: torch.Tensor | None = None,
                     out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """One attention layer: QK-norm + RoPE of raw q, k, then causal attention with ``window``."""
+    """One attention layer: QK-norm + RoPE of raw q, k, then causal attention with ``window``
+    (two calls: attn_qknorm_rope writes the normalised q and k, attn_fwd reads them)."""
     qn, kn = qknorm_rope(q, k, cos, sin, eps, qn, kn)
     return attn_fwd(qn, kn, v, window=window, causal=True, out=out, lse=lse)
