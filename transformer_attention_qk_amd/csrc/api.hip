@@ -99,6 +99,7 @@ int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, con
   int64_t n = 0;
   if (int rc = check_shape(B, H, T, d, &n)) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ATTN_ERR_ARG;
+  if (2 * (int64_t)B * H > 0x7fffffff) return ATTN_ERR_SHAPE;  // q's and k's heads, as int
   if ((q && !aligned16(q)) || !aligned16(k) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
       !aligned16(cos_tab) || !aligned16(sin_tab))
     return ATTN_ERR_ALIGN;
@@ -213,6 +214,7 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, v
     return rc;
   if (!k) return ATTN_ERR_NULL;
   if (!aligned16(k)) return ATTN_ERR_ALIGN;
+  if (2 * (int64_t)B * H > 0x7fffffff) return ATTN_ERR_SHAPE;
   const int64_t bytes = n * 2;
   if (k_work != k && overlap(k_work, bytes, k, bytes)) return ATTN_ERR_ALIAS;
   if (overlap(k_work, bytes, q, bytes) || overlap(k_work, bytes, v, bytes) ||

@@ -761,22 +761,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       break;
     }
     {
-      // (QKN) the rotation factors of the new rows are loaded here; held through the item's
-      // last tile step they would push that code past the register budget.
+      // (QKN) the rotation factors of the new rows are loaded here (held through the item's
+      // last tile step they would push that code past the register budget); the previous
+      // item's stores go out while they are in flight.
       w.load_rope(nq0, cos_tab, sin_tab, rope);
+      w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
       bf16x8 xf[C::KSTEPS];
       w.load_q_lds(qbuf, xf);
       w.set_q(xf, rope, nq0, eps);
     }
-    w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
     ++k;
     bh = nbh;
     q0 = nq0;
     tb = ntb;
     te = nte;
     w.set_item(q0);
-    // Every wave has its Q fragments before anyone issues the next Q block into the buffer.
-    __syncthreads();
+    // Every wave must have read its Q rows before any wave issues the next Q block into the
+    // buffer, in the new item's last tile step. A tile step ends with a barrier, so one is
+    // needed here only when that last step is the item's first.
+    if (te - tb == 1) __syncthreads();
   }
 }
 

@@ -9,7 +9,8 @@
 // The prologue is bound by HBM: it reads and writes every element of q and k once (8*d bytes per
 // token per head in bf16). Each row of d elements is handled by a group of L lanes; a lane holds E
 // elements of the first half and the E matching elements of the second half, so the rotation is
-// lane-local and only the sum of squares crosses lanes (xor shuffles inside the group).
+// lane-local and only the sum of squares crosses lanes (xor shuffles inside the group). The
+// rotation factors of a position are loaded once for several heads.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -76,38 +77,30 @@ struct Vec<float, 4> {
 template <typename Elem>
 constexpr int kE = (sizeof(Elem) == 2) ? 8 : 4;
 
-// Rows [0, q_rows) are rows of q, rows [q_rows, q_rows + rows) rows of k (q_rows = 0: k only).
-template <typename Elem, int D>
+// Rows are grouped by position: a block handles TPB positions t of R heads, where the heads are
+// q's B*H heads (when q is given) followed by k's. A row group of L lanes loads the rotation
+// factors of its position once and applies them to its R rows, and every lane issues all of its
+// loads before the first arithmetic, so each lane has R row loads and the table loads in
+// flight at once.
+template <typename Elem, int D, int R>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const Elem* __restrict__ q, const Elem* __restrict__ k, Elem* q_out, Elem* k_out,
-    const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, int64_t q_rows,
-    int64_t rows, int T, float eps) {
+    const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, int heads_q,
+    int heads, int T, int t_blocks, float eps) {
   constexpr int E = kE<Elem>;
   constexpr int HALF = D / 2;
   static_assert(HALF % E == 0, "half head dim must be a multiple of the lane vector");
   constexpr int L = HALF / E;  // lanes per row (1, 2, 4, 8 or 16)
-  constexpr int ROWS_PER_BLOCK = 256 / L;
-  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / L;
-  const int sub = threadIdx.x % L;
-  // Every lane of a row group shares `row`, so a group is either fully active or fully inactive
-  // and the xor shuffles below never read a lane of another row.
-  if (row >= q_rows + rows) return;
-  const bool is_q = row < q_rows;
-  const int64_t r = is_q ? row : row - q_rows;
-  const Elem* src = (is_q ? q : k) + r * D;
-  Elem* dst = (is_q ? q_out : k_out) + r * D;
-  const int t = (int)(r % T);
+  constexpr int TPB = 256 / L;  // positions per block
+  const int tb = (int)(blockIdx.x % (unsigned)t_blocks);
+  const int h0 = (int)(blockIdx.x / (unsigned)t_blocks) * R;
+  const int t = tb * TPB + (int)threadIdx.x / L;
+  const int sub = (int)threadIdx.x % L;
+  // All L lanes of a row group share t, so a group is either fully active or fully inactive and
+  // the xor shuffles below never read a lane of another row.
+  if (t >= T) return;
   const int j0 = sub * E;
-
-  float x1[E], x2[E];
-  Vec<Elem, E>::load(src + j0, x1);
-  Vec<Elem, E>::load(src + HALF + j0, x2);
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < E; ++i) ss = fmaf(x1[i], x1[i], fmaf(x2[i], x2[i], ss));
-#pragma unroll
-  for (int o = L / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+  const int total = heads_q + heads;
 
   float c[E], s[E];
   const float* ct = cos_tab + (int64_t)t * HALF + j0;
@@ -117,30 +110,56 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     Vec<float, 4>::load(ct + i, c + i);
     Vec<float, 4>::load(st + i, s + i);
   }
-  float y1[E], y2[E];
+  float x1[R][E], x2[R][E];
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const float a = x1[i] * rinv;
-    const float b = x2[i] * rinv;
-    y1[i] = fmaf(a, c[i], b * s[i]);
-    y2[i] = fmaf(b, c[i], -(a * s[i]));
+  for (int r = 0; r < R; ++r) {
+    const int h = h0 + r;  // block-uniform
+    if (h < total) {
+      const Elem* src = (h < heads_q ? q + (int64_t)h * T * D : k + (int64_t)(h - heads_q) * T * D) +
+                        (int64_t)t * D;
+      Vec<Elem, E>::load(src + j0, x1[r]);
+      Vec<Elem, E>::load(src + HALF + j0, x2[r]);
+    }
   }
-  Vec<Elem, E>::store(dst + j0, y1);
-  Vec<Elem, E>::store(dst + HALF + j0, y2);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int h = h0 + r;
+    if (h >= total) break;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) ss = fmaf(x1[r][i], x1[r][i], fmaf(x2[r][i], x2[r][i], ss));
+#pragma unroll
+    for (int o = L / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    float y1[E], y2[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float a = x1[r][i] * rinv;
+      const float b = x2[r][i] * rinv;
+      y1[i] = fmaf(a, c[i], b * s[i]);
+      y2[i] = fmaf(b, c[i], -(a * s[i]));
+    }
+    Elem* dst = (h < heads_q ? q_out + (int64_t)h * T * D : k_out + (int64_t)(h - heads_q) * T * D) +
+                (int64_t)t * D;
+    Vec<Elem, E>::store(dst + j0, y1);
+    Vec<Elem, E>::store(dst + HALF + j0, y2);
+  }
 }
 
 template <typename Elem, int D>
 static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out, void* k_out,
                                        const float* cos_tab, const float* sin_tab, int B, int H,
                                        int T, float eps, hipStream_t stream) {
+  constexpr int R = 2;  // rows per lane (measured best of 1, 2, 4, 8 on MI355X)
   constexpr int L = (D / 2) / kE<Elem>;
-  constexpr int ROWS_PER_BLOCK = 256 / L;
-  const int64_t rows = (int64_t)B * H * T;
-  const int64_t q_rows = (q != nullptr) ? rows : 0;
-  const int64_t grid = (q_rows + rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
-  hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D>), dim3((unsigned)grid), dim3(256), 0, stream,
+  constexpr int TPB = 256 / L;
+  const int heads = B * H;
+  const int heads_q = (q != nullptr) ? heads : 0;
+  const int t_blocks = (T + TPB - 1) / TPB;
+  const int64_t grid = (int64_t)t_blocks * ((heads_q + heads + R - 1) / R);
+  hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
                      (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, cos_tab, sin_tab,
-                     q_rows, rows, T, eps);
+                     heads_q, heads, T, t_blocks, eps);
   return hipGetLastError();
 }
 
