@@ -74,6 +74,13 @@ struct FwdCfg {
   static constexpr int STREAM_LDS = NSTAGE * 2 * TILE_BYTES + Q_BYTES;
   static constexpr int DMA_PER_TILE = 2 * LPT;             // direct loads per thread per stage
   static constexpr int DMA_PER_Q = Q_BYTES / (1024 * 4);   // direct loads per thread per Q block
+  // Rotation factors staged for an item transition of the QKN streaming kernel: table rows
+  // (cos, then sin, d/2 floats each) of the 8 bases q0 + 16 m and of the 16 offsets e < 16,
+  // each table's part padded to whole 1 KiB runs; they fit in the K half of a ring stage.
+  static constexpr int ROPE_ROWS = 8 + 16;
+  static constexpr int ROPE_PART = (ROPE_ROWS * D * 2 + 1023) / 1024 * 1024;  // bytes per table
+  static constexpr int ROPE_RUNS = 2 * ROPE_PART / 1024;
+  static_assert(2 * ROPE_PART <= TILE_BYTES, "staged rotation factors must fit in a K tile");
   // Tile kernel: K ring (2 tiles), then V ring (2 tiles).
   static constexpr int TILE_LDS = 4 * TILE_BYTES;
 };
@@ -283,6 +290,36 @@ struct WaveTile {
         for (int h = 0; h < 2; ++h) {
           r.c[s][h] = __builtin_bit_cast(f32x4, buffer_load16(rc, off + 64 * s + 16 * h));
           r.s[s][h] = __builtin_bit_cast(f32x4, buffer_load16(rs, off + 64 * s + 16 * h));
+        }
+    }
+  }
+  // The same factors from the rows staged in LDS at rope_lds (layout above): the row's position
+  // q0 + 32 wave + l splits into the base q0 + 16 m, m = 2 wave + l / 16, and the offset
+  // e = l % 16, and the angle-addition formulas
+  //   cos((b + e) w) = cos(b w) cos(e w) - sin(b w) sin(e w)
+  //   sin((b + e) w) = sin(b w) cos(e w) + cos(b w) sin(e w)
+  // give the factors in fp32 from the two table rows.
+  __device__ __forceinline__ void rope_from_lds(const char* rope_lds, Rope& r) const {
+    if constexpr (QKN) {
+      constexpr int RB = D * 2;  // bytes of one staged row (d/2 floats)
+      const int ln = lane_now();
+      const int l = ln & 31, col = 32 * (ln >> 5);  // byte offset of column 8 hi
+      const char* cb = rope_lds + (2 * wave + (l >> 4)) * RB + col;
+      const char* cl = rope_lds + (8 + (l & 15)) * RB + col;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS / 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int o = 64 * s + 16 * h;
+          const f32x4 c_b = *reinterpret_cast<const f32x4*>(cb + o);
+          const f32x4 s_b = *reinterpret_cast<const f32x4*>(cb + C::ROPE_PART + o);
+          const f32x4 c_l = *reinterpret_cast<const f32x4*>(cl + o);
+          const f32x4 s_l = *reinterpret_cast<const f32x4*>(cl + C::ROPE_PART + o);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r.c[s][h][e] = fmaf(c_b[e], c_l[e], -(s_b[e] * s_l[e]));
+            r.s[s][h][e] = fmaf(s_b[e], c_l[e], c_b[e] * s_l[e]);
+          }
         }
     }
   }
@@ -605,6 +642,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     }
   };
 
+  // (QKN) Direct loads of the rotation-factor rows of the item at q0 into the K half of stage st
+  // (run r of the ROPE_RUNS: table r / (runs per table), 1 KiB run within it; chunks past the
+  // staged rows are sent out of range). Rows past T are clamped to T - 1.
+  auto dma_rope = [&](int q0, unsigned st) {
+    constexpr int RPP = C::ROPE_PART / 1024;     // runs per table
+    constexpr int CPR = D / 8;                   // 16-byte chunks per staged row
+    const u32x4 rc = head_rsrc_words((const bf16*)cos_tab, T * D * 2);
+    const u32x4 rs = head_rsrc_words((const bf16*)sin_tab, T * D * 2);
+    const uint32_t base = lds0 + st * (2 * C::TILE_BYTES);
+    for (int r = w.wave; r < C::ROPE_RUNS; r += 4) {  // wave-uniform
+      const int part = r / RPP, run = r % RPP;
+      const int p = run * 64 + w.lane;
+      const int row_i = p / CPR, col = p % CPR;
+      const int row = row_i < 8 ? min(q0 + 16 * row_i, T - 1) : min(row_i - 8, T - 1);
+      const uint32_t off = row_i < C::ROPE_ROWS ? (uint32_t)(row * (D * 2) + 16 * col) : kOutOfRange;
+      dma16(part ? rs : rc, base + part * C::ROPE_PART + run * 1024, off);
+    }
+  };
+
   // The K/V stream: one tile per step, across items. The cursor holds the next tile to issue
   // (pt of [pt, pte) of the item of rank index pk), that head's K and V buffer resources and the
   // stage the tile goes to. Once the items run out, out-of-range loads keep the count per step
@@ -687,7 +743,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     // code, where the registers of the rotation factors are free.
     auto body = [&](auto has_next_c, int t, f32x16(&cur)[2], f32x16(&nxt)[2]) {
       constexpr bool has_next = decltype(has_next_c)::value;
-      if (!has_next && more) dma_q(nbh, nq0);
+      if (!has_next && more) {
+        dma_q(nbh, nq0);
+        if constexpr (QKN) {
+          // The K half of this stage is free once tile t's keys are consumed: in the previous
+          // step, or in this item's prologue when t is its only tile (then after a barrier).
+          if (te - tb == 1) __syncthreads();
+          dma_rope(nq0, st_comp);
+        }
+      }
       issue_next();
       const char* kn = smem + ((st_comp + 1) & (C::NSTAGE - 1)) * (2 * C::TILE_BYTES);
       const char* vc = smem + st_comp * (2 * C::TILE_BYTES) + C::TILE_BYTES;
@@ -761,25 +825,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       break;
     }
     {
-      // (QKN) the rotation factors of the new rows are loaded here (held through the item's
-      // last tile step they would push that code past the register budget); the previous
-      // item's stores go out while they are in flight.
-      w.load_rope(nq0, cos_tab, sin_tab, rope);
-      w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
+      // (QKN) the new rows' rotation factors were staged in the K half of the last tile's stage
+      // during the last step.
+      w.rope_from_lds(smem + ((st_comp + C::NSTAGE - 1) & (C::NSTAGE - 1)) * (2 * C::TILE_BYTES),
+                      rope);
       bf16x8 xf[C::KSTEPS];
       w.load_q_lds(qbuf, xf);
       w.set_q(xf, rope, nq0, eps);
     }
+    w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
     ++k;
     bh = nbh;
     q0 = nq0;
     tb = ntb;
     te = nte;
     w.set_item(q0);
-    // Every wave must have read its Q rows before any wave issues the next Q block into the
-    // buffer, in the new item's last tile step. A tile step ends with a barrier, so one is
-    // needed here only when that last step is the item's first.
-    if (te - tb == 1) __syncthreads();
+    // Every wave has read its Q rows and rotation factors before any wave issues loads into the
+    // Q buffer (the new item's last step) or into that stage (its first step).
+    if (QKN || te - tb == 1) __syncthreads();
   }
 }
 
