@@ -254,10 +254,8 @@ struct WaveTile {
   // (bitwise operators: the operands are cheap scalar tests, evaluated without branches)
   __device__ __forceinline__ bool fast(int t) const { return full(t, 0) & full(t, 1); }
   __device__ __forceinline__ bool any(int t) const { return active(t, 0) | active(t, 1); }
-  // Tiles t and t + 1 both fully visible to all of this wave's queries.
-  __device__ __forceinline__ bool fast2(int t) const {
-    return (t * C::BN >= f_lo) & (t * C::BN + 2 * C::BN <= f_hi);
-  }
+  // Both blocks of tile t computed for this wave (some keys may still be masked).
+  __device__ __forceinline__ bool act2(int t) const { return active(t, 0) & active(t, 1); }
 
   // Rotation factors of the lane's Q row at the frequencies it holds (QKN only): cos and sin at
   // columns 16 s + 8 hi .. +8 for s < KSTEPS/2, as 16-byte loads.
@@ -757,7 +755,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       const char* vc = smem + st_comp * (2 * C::TILE_BYTES) + C::TILE_BYTES;
       bf16x8 pf[2][2];
       float mx = -INFINITY;
-      if (has_next && w.fast2(t)) {
+      // Tile t's blocks that this wave does not see hold -inf scores (zero weights), so its
+      // exponentials and P V run unconditionally whenever tile t+1 is computed in full.
+      if (has_next && w.fast(t + 1)) {
         w.template scores<true, true>(kn, t + 1, nxt);
         w.exps(cur, pf);
         w.template pv<true>(vc, t, pf);
@@ -779,6 +779,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
           if (j + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
           if constexpr (!QKN) __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
         }
+      } else if (has_next && w.act2(t + 1)) {
+        // tile t+1 on a mask edge: both blocks computed, then masked
+        w.template scores<true, true>(kn, t + 1, nxt);
+        w.exps(cur, pf);
+        w.template pv<true>(vc, t, pf);
+        mx = w.template mask_max<false>(t + 1, nxt);
       } else if constexpr (has_next) {
         w.template scores<false, true>(kn, t + 1, nxt);
         if (w.any(t)) {
