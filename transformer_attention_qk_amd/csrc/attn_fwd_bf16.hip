@@ -755,43 +755,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       const char* vc = smem + st_comp * (2 * C::TILE_BYTES) + C::TILE_BYTES;
       bf16x8 pf[2][2];
       float mx = -INFINITY;
-      // Tile t's blocks that this wave does not see hold -inf scores (zero weights), so its
-      // exponentials and P V run unconditionally whenever tile t+1 is computed in full.
-      if (has_next && w.fast(t + 1)) {
+      // Every step with a next tile runs the same software pipeline: the scores of both blocks
+      // of tile t+1 are computed (a block this wave does not see costs its MFMAs, which keeps one
+      // code path and the accumulators in fixed registers) and then masked unless the tile is
+      // fully visible; tile t's blocks that the wave does not see hold -inf scores (zero
+      // weights), so its exponentials and P V need no guards.
+      if constexpr (has_next) {
         w.template scores<true, true>(kn, t + 1, nxt);
         w.exps(cur, pf);
         w.template pv<true>(vc, t, pf);
-        mx = w.template mask_max<true>(t + 1, nxt);
-        // Phase A: the K fragment reads of t+1 go out first, then the score MFMAs of t+1
-        // alternate with the exponentials of t.
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * C::KSTEPS, 0);
-#pragma unroll
-        for (int j = 0; j < 2 * C::KSTEPS; ++j) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, (QKN ? 64 : 96) / (2 * C::KSTEPS), 0);
-        }
-        // Phase B: the P V MFMAs of t, each with its V reads issued two MFMAs ahead, alternate
-        // with the mask and maximum of t+1.
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
-#pragma unroll
-        for (int j = 0; j < 4 * C::DB; ++j) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          if (j + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-          if constexpr (!QKN) __builtin_amdgcn_sched_group_barrier(kSchedVALU, 3, 0);
-        }
-      } else if (has_next && w.act2(t + 1)) {
-        // tile t+1 on a mask edge: both blocks computed, then masked
-        w.template scores<true, true>(kn, t + 1, nxt);
-        w.exps(cur, pf);
-        w.template pv<true>(vc, t, pf);
-        mx = w.template mask_max<false>(t + 1, nxt);
-      } else if constexpr (has_next) {
-        w.template scores<false, true>(kn, t + 1, nxt);
-        if (w.any(t)) {
-          w.exps(cur, pf);
-          w.template pv<false>(vc, t, pf);
-        }
-        mx = w.template mask_max<false>(t + 1, nxt);
+        if (w.fast(t + 1))
+          mx = w.template mask_max<true>(t + 1, nxt);
+        else
+          mx = w.template mask_max<false>(t + 1, nxt);
       } else {
         if (w.any(t)) {
           w.exps(cur, pf);
