@@ -364,8 +364,10 @@ struct WaveTile {
         for (int e = 0; e < 8; ++e) ss = fmaf(x[s][e], x[s][e], ss);
       }
       ss = pair_sum(ss);
+      // v_rsq_f32 (about 1 ulp) is ample here: the row is rounded to bf16 right after.
       const float rinv = (q_row(q0) < T)
-                             ? (kLog2e * (1.0f / sqrtf((float)D))) / sqrtf(ss * (1.0f / D) + eps)
+                             ? (kLog2e * (1.0f / sqrtf((float)D))) *
+                                   __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps)
                              : 0.f;
 #pragma unroll
       for (int s = 0; s < C::KSTEPS / 2; ++s) {
