@@ -694,23 +694,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     }
   };
 
-  // Workgroup prologue: stream tiles 0 and 1 and the first item's Q, then tile 2 in flight. The
-  // wait for Q is a compiler-visible s_waitcnt vmcnt(0), so the compiler puts no wait of its own
-  // inside the loop (such a wait would also stall on the tiles in flight).
+  // Workgroup prologue: stream tiles 0 and 1 and the first item's Q (and, QKN, its rotation
+  // rows into the K half of the last stage, which the stream reaches only in the first tile
+  // step), then tile 2 in flight. The wait is a compiler-visible s_waitcnt vmcnt(0), so the
+  // compiler puts no wait of its own inside the loop (such a wait would also stall on the tiles
+  // in flight).
   int k = 0, bh, q0, tb, te;
   decode(rank_of(0), bh, q0, tb, te);
   w.set_item(q0);
   issue_next();
   issue_next();
+  if constexpr (QKN) dma_rope(q0, C::NSTAGE - 1);
   typename WaveTile<D, MODE, QKN>::Rope rope;
   {
     bf16x8 xf[C::KSTEPS];
     w.load_q_global(head_rsrc(Q + (int64_t)bh * T * D, slab), q0, xf);
-    w.load_rope(q0, cos_tab, sin_tab, rope);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    w.rope_from_lds(smem + (C::NSTAGE - 1) * (2 * C::TILE_BYTES), rope);
     w.set_q(xf, rope, q0, eps);
   }
-  __syncthreads();
+  // (QKN) every wave has read the rotation rows before the first tile step loads into that stage
+  if constexpr (QKN) __syncthreads();
   issue_next();
   unsigned st_comp = 0;  // stage of the tile being consumed
 
