@@ -7,10 +7,10 @@
 // rotate-then-normalise order, because the rotation keeps each row's sum of squares.
 //
 // The prologue is bound by HBM: it reads and writes every element of q and k once (8*d bytes per
-// token per head in bf16). Each row of d elements is handled by a group of L lanes; a lane holds E
-// elements of the first half and the E matching elements of the second half, so the rotation is
-// lane-local and only the sum of squares crosses lanes (xor shuffles inside the group). The
-// rotation factors of a position are loaded once for several heads.
+// token per head in bf16). Each row of d elements is handled by a group of lanes, one 16-byte
+// chunk per lane, so every load and store of a wave covers whole rows; the rotation partners swap
+// chunks and the sum of squares crosses the group by xor shuffles. The rotation factors of a
+// position are loaded once for several heads.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -78,10 +78,11 @@ template <typename Elem>
 constexpr int kE = (sizeof(Elem) == 2) ? 8 : 4;
 
 // Rows are grouped by position: a block handles TPB positions t of R heads, where the heads are
-// q's B*H heads (when q is given) followed by k's. A row group of L lanes loads the rotation
-// factors of its position once and applies them to its R rows, and every lane issues all of its
-// loads before the first arithmetic, so each lane has R row loads and the table loads in
-// flight at once.
+// q's B*H heads (when q is given) followed by k's. A row is handled by L = d / E lanes, lane i
+// holding the row's i-th 16-byte chunk, so a wave's loads and stores cover whole rows. The
+// element j < d/2 and its rotation partner j + d/2 sit in lanes i and i ^ (L/2), which swap
+// their chunks with one xor shuffle per 32-bit word; the sum of squares crosses the L lanes by
+// xor shuffles too. A row group loads the rotation factors of its position once for its R rows.
 template <typename Elem, int D, int R>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const Elem* __restrict__ q, const Elem* __restrict__ k, Elem* q_out, Elem* k_out,
@@ -89,9 +90,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     int heads, int T, int t_blocks, float eps) {
   constexpr int E = kE<Elem>;
   constexpr int HALF = D / 2;
-  static_assert(HALF % E == 0, "half head dim must be a multiple of the lane vector");
-  constexpr int L = HALF / E;  // lanes per row (1, 2, 4, 8 or 16)
+  constexpr int L = D / E;      // lanes per row (2 .. 32)
   constexpr int TPB = 256 / L;  // positions per block
+  constexpr int W = E * sizeof(Elem) / 4;  // 32-bit words per chunk
   const int tb = (int)(blockIdx.x % (unsigned)t_blocks);
   const int h0 = (int)(blockIdx.x / (unsigned)t_blocks) * R;
   const int t = tb * TPB + (int)threadIdx.x / L;
@@ -99,7 +100,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   // All L lanes of a row group share t, so a group is either fully active or fully inactive and
   // the xor shuffles below never read a lane of another row.
   if (t >= T) return;
-  const int j0 = sub * E;
+  const bool first = sub < L / 2;
+  const int j0 = (sub % (L / 2)) * E;  // frequency of the chunk's first element
   const int total = heads_q + heads;
 
   float c[E], s[E];
@@ -110,39 +112,42 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     Vec<float, 4>::load(ct + i, c + i);
     Vec<float, 4>::load(st + i, s + i);
   }
-  float x1[R][E], x2[R][E];
+  u32x4 raw[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = h0 + r;  // block-uniform
     if (h < total) {
       const Elem* src = (h < heads_q ? q + (int64_t)h * T * D : k + (int64_t)(h - heads_q) * T * D) +
-                        (int64_t)t * D;
-      Vec<Elem, E>::load(src + j0, x1[r]);
-      Vec<Elem, E>::load(src + HALF + j0, x2[r]);
+                        (int64_t)t * D + sub * E;
+      raw[r] = *reinterpret_cast<const u32x4*>(src);
     }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = h0 + r;
     if (h >= total) break;
+    u32x4 part;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) part[wd] = (uint32_t)__shfl_xor((int)raw[r][wd], L / 2);
+    float x[E], xp[E];
+    Vec<Elem, E>::load(reinterpret_cast<const Elem*>(&raw[r]), x);
+    Vec<Elem, E>::load(reinterpret_cast<const Elem*>(&part), xp);
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < E; ++i) ss = fmaf(x1[r][i], x1[r][i], fmaf(x2[r][i], x2[r][i], ss));
+    for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
 #pragma unroll
     for (int o = L / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
     const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-    float y1[E], y2[E];
+    float y[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const float a = x1[r][i] * rinv;
-      const float b = x2[r][i] * rinv;
-      y1[i] = fmaf(a, c[i], b * s[i]);
-      y2[i] = fmaf(b, c[i], -(a * s[i]));
+      const float a = x[i] * rinv, b = xp[i] * rinv;
+      // first half: x_j cos + x_{j+h} sin; second half: -x_j sin + x_{j+h} cos
+      y[i] = first ? fmaf(a, c[i], b * s[i]) : fmaf(a, c[i], -(b * s[i]));
     }
     Elem* dst = (h < heads_q ? q_out + (int64_t)h * T * D : k_out + (int64_t)(h - heads_q) * T * D) +
-                (int64_t)t * D;
-    Vec<Elem, E>::store(dst + j0, y1);
-    Vec<Elem, E>::store(dst + HALF + j0, y2);
+                (int64_t)t * D + sub * E;
+    Vec<Elem, E>::store(dst, y);
   }
 }
 
@@ -150,8 +155,8 @@ template <typename Elem, int D>
 static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out, void* k_out,
                                        const float* cos_tab, const float* sin_tab, int B, int H,
                                        int T, float eps, hipStream_t stream) {
-  constexpr int R = 2;  // rows per lane (measured best of 1, 2, 4, 8 on MI355X)
-  constexpr int L = (D / 2) / kE<Elem>;
+  constexpr int R = 2;  // rows per lane
+  constexpr int L = D / kE<Elem>;
   constexpr int TPB = 256 / L;
   const int heads = B * H;
   const int heads_q = (q != nullptr) ? heads : 0;
