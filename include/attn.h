@@ -11,7 +11,13 @@
  *          sections "O que a Atenção Calcula", "A Máscara Causal", "Escalonamento por sqrt(d_k)".
  *
  * Conventions for every entry point:
- *   - Tensors are dense, contiguous, row-major [B][H][T][d] (batch, head, token, channel).
+ *   - Tensors are dense and contiguous. The entry points without a suffix take row-major
+ *     [B][H][T][d] (batch, head, token, channel) tensors whose k and v have as many heads as q.
+ *     Their _ex variants add H_kv and layout: q and out are [B, H, T, d], k and v [B, H_kv, T, d]
+ *     with H_kv dividing H (grouped-query attention: q head h attends with kv head
+ *     h / (H / H_kv)), all stored in the order that layout names (attn_layout). lse is always
+ *     [B][H][T]. The call without a suffix equals its _ex variant with H_kv = H and
+ *     ATTN_LAYOUT_BHTD.
  *   - Pointers named as device pointers must point to device memory of the current HIP device;
  *     the caller allocates and frees all of them. The library allocates no memory, keeps no
  *     mutable global state beyond a per-device cache of how many workgroups the GPU holds at
@@ -33,6 +39,14 @@
 extern "C" {
 #endif
 
+/* Storage order of q, k, v and out in the _ex entry points. */
+typedef enum attn_layout {
+  ATTN_LAYOUT_BHTD = 0, /* [B][H][T][d]: each head's rows are contiguous */
+  ATTN_LAYOUT_BTHD = 1  /* [B][T][H][d]: the order the projections produce in [HABR]
+                           `CausalSelfAttention.forward` (q, k, v viewed as (B, T, heads, d)
+                           before the attention call); row stride H * d (H_kv * d for k, v) */
+} attn_layout;
+
 /* Element type of q, k, v and out (the prologue and attention compute in fp32 internally). */
 typedef enum attn_dtype {
   ATTN_BF16 = 0, /* bfloat16; matrix products on bf16 MFMA with fp32 accumulation */
@@ -42,13 +56,14 @@ typedef enum attn_dtype {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* B, H or T < 1, or an element count that overflows int64 */
+  ATTN_ERR_SHAPE = 2,       /* B, H, H_kv or T < 1, H_kv not dividing H, or a tensor too large */
   ATTN_ERR_HEAD_DIM = 3,    /* head dim d not supported for this entry point and dtype */
   ATTN_ERR_DTYPE = 4,       /* dtype is not an attn_dtype value */
   ATTN_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
   ATTN_ERR_WINDOW = 6,      /* causal is not 0/1, or causal == 0 with window >= 0 */
   ATTN_ERR_ALIAS = 7,       /* out or lse overlaps an input it must not overlap */
-  ATTN_ERR_ARG = 8,         /* another argument is out of range (eps, base, pattern, n_layer) */
+  ATTN_ERR_ARG = 8,         /* another argument is out of range (eps, base, pattern, n_layer,
+                               layout) */
   ATTN_ERR_HIP = 9          /* the HIP runtime refused the launch */
 };
 
@@ -168,6 +183,38 @@ int attn_fwd_qnorm(const void* q, const void* k, const void* v, void* out, float
 int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, void* out,
                     float* lse, const float* cos_tab, const float* sin_tab, int B, int H, int T,
                     int d, float eps, int window, int causal, int dtype, void* stream);
+
+/*
+ * Grouped-query and [B][T][H][d] variants of the four entry points above ([HABR] `GPTConfig`
+ * and `CausalSelfAttention`: n_kv_head key/value heads, n_kv_head dividing n_head, each shared
+ * by a group of n_head / n_kv_head query heads; q, k, v viewed in the (B, T, heads, d) order of
+ * the projections before the attention call). Arguments, rules and
+ * results are those of the entry point without the suffix, with these differences:
+ *   H_kv     heads of k, v (and k_out, k_work); H_kv >= 1 and H % H_kv == 0, else
+ *            ATTN_ERR_SHAPE. q, out and q_out have H heads; lse is [B][H][T].
+ *   layout   an attn_layout value (else ATTN_ERR_ARG); every tensor argument except lse, cos_tab
+ *            and sin_tab is stored in that order.
+ * Query head h of batch b attends with kv head h / (H / H_kv) of batch b. The attn_qknorm_rope_ex
+ * prologue normalises and rotates the B*H rows of q and the B*H_kv rows of k per position.
+ * The bf16 attention kernels address one head's rows through 32-bit byte offsets: for
+ * ATTN_BF16, (T + 128) * (largest row stride in bytes) must be below 2^31, else ATTN_ERR_SHAPE
+ * (row stride: d * 2 for ATTN_LAYOUT_BHTD, H * d * 2 for q and H_kv * d * 2 for k, v in
+ * ATTN_LAYOUT_BTHD).
+ */
+int attn_qknorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
+                        const float* cos_tab, const float* sin_tab, int B, int H, int H_kv, int T,
+                        int d, int layout, float eps, int dtype, void* stream);
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                int H_kv, int T, int d, int layout, int window, int causal, int dtype,
+                void* stream);
+int attn_fwd_qnorm_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                      const float* cos_tab, const float* sin_tab, int B, int H, int H_kv, int T,
+                      int d, int layout, float eps, int window, int causal, int dtype,
+                      void* stream);
+int attn_fwd_qknorm_ex(const void* q, const void* k, const void* v, void* k_work, void* out,
+                       float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
+                       int H_kv, int T, int d, int layout, float eps, int window, int causal,
+                       int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,9 @@ R4  ``window = W >= 0`` makes key j visible to query i iff 0 <= i - j <= W. This
     means unlimited, as in [HABR] ``GPT.estimate_flops``.
 R5  ``causal = False`` means every key is visible (no window is allowed then).
 R6  LSE is the natural-log logsumexp of the scaled scores over the visible keys.
+R13 Grouped-query attention ([HABR] ``GPTConfig.n_kv_head`` and ``CausalSelfAttention``: k and v
+    carry n_kv_head heads, n_kv_head divides n_head). The pages do not say which query heads share
+    a kv head; consecutive groups do: query head h uses kv head h // (n_head // n_kv_head).
 
 Parity pins: the tests under ``tests/test_oracle_*.py`` check every function here against
 closed forms, the worked example of [GEOM], brute force and library special cases.
@@ -120,6 +123,13 @@ def qknorm_rope(q: np.ndarray, k: np.ndarray, eps: float = EPS_DEFAULT,
     return rope_apply(rms_norm(q, eps), cos, sin), rope_apply(rms_norm(k, eps), cos, sin)
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """Key/value head that query head h of H attends with when k and v have H_kv heads (R13)."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("the kv head count must divide the query head count")
+    return h // (H // H_kv)
+
+
 def visible(i: np.ndarray, j: np.ndarray, window: int = -1, causal: bool = True) -> np.ndarray:
     """Boolean visibility of key j to query i (broadcasting).
 
@@ -151,7 +161,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int = -1, cau
               rows: np.ndarray | None = None, block: int = 256) -> tuple[np.ndarray, np.ndarray]:
     """softmax(q k^T / sqrt(d) + mask) v and its logsumexp, in fp64.
 
-    q, k, v: [B, H, T, d]. Returns (O, LSE) with O [B, H, R, d] and LSE [B, H, R], where R = T,
+    q: [B, H, T, d]; k, v: [B, H_kv, T, d] with H_kv dividing H (R13; H_kv = H is plain
+    multi-head attention). Returns (O, LSE) with O [B, H, R, d] and LSE [B, H, R], where R = T,
     or R = len(rows) when ``rows`` (query indices, applied to every head) is given.
 
     [GEOM] "O que a Atenção Calcula" (softmax(Q K^T / sqrt(d_k)) V: the weights of a row sum to 1
@@ -164,9 +175,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int = -1, cau
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    if q.ndim != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
-        raise ValueError("q, k, v must be [B, H, T, d] with matching B, H, T (and q, k the same d)")
+    if (q.ndim != 4 or k.ndim != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]
+            or v.shape[:3] != k.shape[:3]):
+        raise ValueError("q must be [B, H, T, d] and k, v [B, H_kv, T, d] (q, k the same d)")
     B, H, T, d = q.shape
+    H_kv = k.shape[1]
     dv = v.shape[-1]
     if not causal and window >= 0:
         raise ValueError("a window needs causal=True")
@@ -184,12 +197,13 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int = -1, cau
         vis = visible(ridx[:, None], keys[None, :], window, causal)  # [r, n]
         for b in range(B):
             for h in range(H):
-                s = (q[b, h, ridx] @ k[b, h, lo:hi].T) * scale  # [r, n]
+                g = kv_head(h, H, H_kv)
+                s = (q[b, h, ridx] @ k[b, g, lo:hi].T) * scale  # [r, n]
                 s = np.where(vis, s, -np.inf)
                 m = np.max(s, axis=1, keepdims=True)
                 row_lse = m + np.log(np.sum(np.exp(s - m), axis=1, keepdims=True))
                 p = np.exp(s - row_lse)
-                out[b, h, s0:s0 + ridx.size] = p @ v[b, h, lo:hi]
+                out[b, h, s0:s0 + ridx.size] = p @ v[b, g, lo:hi]
                 lse[b, h, s0:s0 + ridx.size] = row_lse[:, 0]
     return out, lse
 

@@ -330,6 +330,29 @@ def check_sssl_windows(o):
     assert o.sssl_windows(1025, 3, "ss") == [512, 512, 1025]
 
 
+def check_gqa_head_mapping(o, seed=10):
+    """R13: with every value row of kv head g equal to the constant g + 1, each output row is a
+    convex combination of equal rows, so out[b, h] is exactly kv_head(h) + 1 = h // (H / H_kv) + 1
+    whatever q and k are; with H_kv = H the call is plain multi-head attention."""
+    rng = _rng(seed)
+    B, H, T, d = 2, 6, 7, 4
+    q = rng.standard_normal((B, H, T, d))
+    for H_kv in (1, 2, 3, 6):
+        k = rng.standard_normal((B, H_kv, T, d))
+        v = np.broadcast_to((np.arange(H_kv) + 1.0)[None, :, None, None], (B, H_kv, T, 3)).copy()
+        for window in (-1, 2):
+            out, lse = o.attention(q, k, v, window=window)
+            for h in range(H):
+                assert np.allclose(out[:, h], h // (H // H_kv) + 1.0, rtol=0, atol=1e-13), (H_kv, h)
+    # Plain multi-head case: each head equals a one-head call on that head.
+    k = rng.standard_normal((B, H, T, d))
+    v = rng.standard_normal((B, H, T, d))
+    out, lse = o.attention(q, k, v, window=3)
+    for h in (0, 4):
+        o1, l1 = o.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], window=3)
+        assert np.array_equal(out[:, h:h + 1], o1) and np.array_equal(lse[:, h:h + 1], l1)
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_worked_example_qknorm,
@@ -345,4 +368,5 @@ ALL_CHECKS = [
     check_rope_invariants,
     check_norm_rope_commute,
     check_sssl_windows,
+    check_gqa_head_mapping,
 ]

@@ -254,3 +254,136 @@ def test_attn_fwd_qnorm_rejects_before_any_hip_call(lib, name, kw, code):
                             a["B"], a["H"], a["T"], a["d"], a["eps"], a["window"], a["causal"],
                             a["dtype"], a["stream"])
     assert rc == code, (name, rc, lib.attn_strerror(rc))
+
+
+# ---------------------------------------------------------------------------------------------
+# The _ex entry points (grouped-query heads, [B][T][H][d] storage). Every case of the lists above
+# must give the same status through the _ex variant with H_kv = H and the [B][H][T][d] layout,
+# and the new arguments have rules of their own.
+# ---------------------------------------------------------------------------------------------
+
+def _fwd_ex(lib, a):
+    return lib.attn_fwd_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"],
+                           a.get("H_kv", a["H"]), a["T"], a["d"], a.get("layout", 0), a["window"],
+                           a["causal"], a["dtype"], a["stream"])
+
+
+def _qkn_ex(lib, a):
+    return lib.attn_qknorm_rope_ex(a["q"], a["k"], a["qo"], a["ko"], a["cos"], a["sin"], a["B"],
+                                   a["H"], a.get("H_kv", a["H"]), a["T"], a["d"],
+                                   a.get("layout", 0), a["eps"], a["dtype"], a["stream"])
+
+
+def _qnorm_ex(lib, a):
+    return lib.attn_fwd_qnorm_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cos"], a["sin"],
+                                 a["B"], a["H"], a.get("H_kv", a["H"]), a["T"], a["d"],
+                                 a.get("layout", 0), a["eps"], a["window"], a["causal"],
+                                 a["dtype"], a["stream"])
+
+
+def _fused_ex(lib, a):
+    return lib.attn_fwd_qknorm_ex(a["q"], a["k"], a["v"], a["kw"], a["out"], a["lse"], a["cos"],
+                                  a["sin"], a["B"], a["H"], a.get("H_kv", a["H"]), a["T"],
+                                  a["d"], a.get("layout", 0), a["eps"], a["window"], a["causal"],
+                                  a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_attn_fwd_ex_matches_attn_fwd_on_every_case(lib, name, kw, code):
+    assert _fwd_ex(lib, fwd_args(**kw)) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", QKN_CASES, ids=[c[0] for c in QKN_CASES])
+def test_qknorm_rope_ex_matches_qknorm_rope_on_every_case(lib, name, kw, code):
+    assert _qkn_ex(lib, qkn_args(**kw)) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", QNORM_CASES, ids=[c[0] for c in QNORM_CASES])
+def test_attn_fwd_qnorm_ex_matches_attn_fwd_qnorm_on_every_case(lib, name, kw, code):
+    assert _qnorm_ex(lib, fused_args(**kw)) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_attn_fwd_qknorm_ex_matches_attn_fwd_qknorm_on_every_case(lib, name, kw, code):
+    assert _fused_ex(lib, fused_args(**kw)) == code
+
+
+# Far-apart fake pointers for the cases whose tensors are GiBs long.
+_FAR = {n: (i + 1) << 40 for i, n in enumerate(("q", "k", "v", "out", "lse", "cos", "sin"))}
+_FAR_KV = 1 << 29  # k's bytes for B=1, H_kv=2, T=2^20, d=128 bf16
+
+EX_RULES = [
+    ("H_kv=0", dict(H=4, H_kv=0), _lib.ATTN_ERR_SHAPE),
+    ("H_kv=-2", dict(H=4, H_kv=-2), _lib.ATTN_ERR_SHAPE),
+    ("H_kv does not divide H", dict(H=4, H_kv=3), _lib.ATTN_ERR_SHAPE),
+    ("H_kv > H", dict(H=2, H_kv=4), _lib.ATTN_ERR_SHAPE),
+    ("layout 2", dict(layout=2), _lib.ATTN_ERR_ARG),
+    ("layout -1", dict(layout=-1), _lib.ATTN_ERR_ARG),
+    # k has B*H_kv*T*d elements: an out ending inside k's last row aliases it
+    ("out inside the end of a GQA k", dict(H=4, H_kv=2, out=Bp + 2 * 64 * 64 * 2 - 16),
+     _lib.ATTN_ERR_ALIAS),
+    # [B][T][H][d] rows are H*d*2 bytes apart: (T + 128) of them must stay below 2^31 bytes
+    ("bthd slab too large", dict(B=1, H=8, H_kv=2, T=1 << 20, d=128, layout=1, **_FAR),
+     _lib.ATTN_ERR_SHAPE),
+    # with the same sizes, an out placed right after k (whose extent uses H_kv, not H) passes
+    # the overlap checks and stops at the slab rule
+    ("out right after a GQA k", dict(B=1, H=8, H_kv=2, T=1 << 20, d=128, layout=1,
+                                     **dict(_FAR, out=_FAR["k"] + _FAR_KV)), _lib.ATTN_ERR_SHAPE),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", EX_RULES, ids=[c[0] for c in EX_RULES])
+def test_attn_fwd_ex_geometry_rules(lib, name, kw, code):
+    assert _fwd_ex(lib, fwd_args(**kw)) == code, name
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", EX_RULES, ids=[c[0] for c in EX_RULES])
+def test_attn_fwd_qnorm_ex_geometry_rules(lib, name, kw, code):
+    assert _qnorm_ex(lib, fused_args(**kw)) == code, name
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", EX_RULES[:6], ids=[c[0] for c in EX_RULES[:6]])
+def test_qknorm_rope_ex_geometry_rules(lib, name, kw, code):
+    assert _qkn_ex(lib, qkn_args(**kw)) == code, name
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", EX_RULES[:6], ids=[c[0] for c in EX_RULES[:6]])
+def test_attn_fwd_qknorm_ex_geometry_rules(lib, name, kw, code):
+    assert _fused_ex(lib, fused_args(**kw)) == code, name
+
+
+@no_gpu
+def test_qknorm_rope_ex_k_extent_uses_kv_heads(lib):
+    # q has 4 heads, k 1: k's 8 KiB end where k_out starts, so this is no overlap; q_out inside
+    # k's extent is one.
+    a = qkn_args(H=4, H_kv=1, qo=Bp + 64 * 64 * 2 - 16)
+    assert _qkn_ex(lib, a) == _lib.ATTN_ERR_ALIAS
+    a = qkn_args(H=4, H_kv=1, ko=Bp + 64 * 64 * 2, eps=-1.0)
+    assert _qkn_ex(lib, a) == _lib.ATTN_ERR_ARG  # reached the eps rule: no alias found first
+
+
+def test_binding_geometry():
+    """Host-side shape logic of the Python binding (no tensor reaches the library)."""
+    import torch
+    from transformer_attention_qk_amd.ops import _geometry
+    q = torch.empty(2, 8, 128, 64)
+    k = torch.empty(2, 2, 128, 64)
+    assert _geometry(q, k, "bhtd") == (2, 8, 2, 128, 64)
+    assert _geometry(q.transpose(1, 2), k.transpose(1, 2), "bthd") == (2, 8, 2, 128, 64)
+    assert _geometry(None, k, "bhtd") == (2, 2, 2, 128, 64)
+    with pytest.raises(ValueError):
+        _geometry(q, torch.empty(2, 3, 128, 64), "bhtd")  # 3 does not divide 8
+    with pytest.raises(ValueError):
+        _geometry(q, torch.empty(2, 2, 64, 64), "bhtd")  # T differs
+    with pytest.raises(ValueError):
+        _geometry(q, k, "tbhd")
+    with pytest.raises(ValueError):
+        _geometry(q, k, "bthd")  # read as [B, T, H, d], the shapes disagree

@@ -115,3 +115,15 @@ def test_prologue_mutations_are_caught(name, overrides):
     checks = [pins.check_rope_special_values, pins.check_rope_invariants, pins.check_rms_norm,
               pins.check_worked_example_qknorm, pins.check_sssl_windows]
     assert _fails(o, checks), name
+
+
+def _gqa_interleaved(q, k, v, window=-1, causal=True, rows=None, block=256):
+    """Query head h attends with kv head h % H_kv instead of h // (H / H_kv)."""
+    H, H_kv = q.shape[1], k.shape[1]
+    idx = [h % H_kv for h in range(H)]
+    return oracle.attention(q, np.asarray(k)[:, idx], np.asarray(v)[:, idx], window, causal,
+                            rows=rows, block=block)
+
+
+def test_gqa_mapping_mutation_is_caught():
+    assert _fails(_mutant(attention=_gqa_interleaved), [pins.check_gqa_head_mapping])

@@ -32,7 +32,23 @@ SIGNATURES = {
     "attn_fwd_qknorm": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_float,
                                 c_int, c_int, c_int, c_void_p]),
+    "attn_qknorm_rope_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_int,
+                                    c_void_p]),
+    "attn_fwd_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                            c_void_p]),
+    "attn_fwd_qnorm_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                                  c_int, c_int, c_int, c_void_p]),
+    "attn_fwd_qknorm_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                   c_float, c_int, c_int, c_int, c_void_p]),
 }
+
+# storage orders (attn_layout)
+ATTN_LAYOUT_BHTD = 0
+ATTN_LAYOUT_BTHD = 1
 
 # status codes (include/attn.h)
 ATTN_OK = 0

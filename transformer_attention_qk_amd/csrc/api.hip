@@ -19,15 +19,39 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-// Checks B, H, T >= 1 and that B*H*T*d elements stay addressable; returns the element count.
-int check_shape(int B, int H, int T, int d, int64_t* n) {
-  if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
+// Validates one call's shape: B, H, H_kv, T >= 1, H_kv divides H, a known layout, and element
+// counts that stay addressable. Fills dm and the element counts of q (and out) and of k (and v).
+int check_dims(int B, int H, int H_kv, int T, int d, int layout, attn::Dims* dm, int64_t* n_q,
+               int64_t* n_kv) {
+  if (B < 1 || H < 1 || H_kv < 1 || T < 1) return ATTN_ERR_SHAPE;
+  if (H % H_kv != 0) return ATTN_ERR_SHAPE;
+  if (layout != ATTN_LAYOUT_BHTD && layout != ATTN_LAYOUT_BTHD) return ATTN_ERR_ARG;
   const int64_t bh = (int64_t)B * H;
   if (bh > 0x7fffffff) return ATTN_ERR_SHAPE;
   const int64_t rows = bh * T;
   if (rows > kMaxElems / 256) return ATTN_ERR_SHAPE;
-  *n = rows * d;
+  // A row stride of the [B][T][H][d] order (H * d elements) must fit an int.
+  if ((int64_t)H * d > 0x3fffffff) return ATTN_ERR_SHAPE;
+  *n_q = rows * d;
+  *n_kv = (int64_t)B * H_kv * T * d;
+  *dm = attn::Dims{B, H, H_kv, T, d, layout};
   return ATTN_OK;
+}
+
+// Bytes between consecutive rows (tokens) of one head of q and of k.
+int64_t q_row_bytes(const attn::Dims& dm, int eb) {
+  return (int64_t)(dm.layout == ATTN_LAYOUT_BTHD ? dm.H * dm.d : dm.d) * eb;
+}
+int64_t kv_row_bytes(const attn::Dims& dm, int eb) {
+  return (int64_t)(dm.layout == ATTN_LAYOUT_BTHD ? dm.H_kv * dm.d : dm.d) * eb;
+}
+
+// The bf16 attention kernels address one head's rows (plus a query block of padding rows)
+// through 32-bit buffer offsets: (T + 128) row strides must stay below 2^31 bytes.
+bool slab_fits(const attn::Dims& dm) {
+  const int64_t rs = q_row_bytes(dm, 2) > kv_row_bytes(dm, 2) ? q_row_bytes(dm, 2)
+                                                               : kv_row_bytes(dm, 2);
+  return ((int64_t)dm.T + 128) * rs < (int64_t(1) << 31);
 }
 
 int elem_bytes(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
@@ -88,83 +112,95 @@ int attn_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base, v
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos_tab,
-                     const float* sin_tab, int B, int H, int T, int d, float eps, int dtype,
-                     void* stream) {
+int attn_qknorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
+                        const float* cos_tab, const float* sin_tab, int B, int H, int H_kv, int T,
+                        int d, int layout, float eps, int dtype, void* stream) {
   // q and q_out are both given or both NULL (then only k is processed).
   if (!k || !k_out || !cos_tab || !sin_tab || (q == nullptr) != (q_out == nullptr))
     return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  int64_t n = 0;
-  if (int rc = check_shape(B, H, T, d, &n)) return rc;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_dims(B, H, H_kv, T, d, layout, &dm, &n_q, &n_kv)) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ATTN_ERR_ARG;
   if (2 * (int64_t)B * H > 0x7fffffff) return ATTN_ERR_SHAPE;  // q's and k's heads, as int
   if ((q && !aligned16(q)) || !aligned16(k) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
       !aligned16(cos_tab) || !aligned16(sin_tab))
     return ATTN_ERR_ALIGN;
-  const int64_t bytes = n * elem_bytes(dtype);
-  if (k_out != k && overlap(k_out, bytes, k, bytes)) return ATTN_ERR_ALIAS;
+  const int64_t qb = n_q * elem_bytes(dtype), kb = n_kv * elem_bytes(dtype);
+  if (k_out != k && overlap(k_out, kb, k, kb)) return ATTN_ERR_ALIAS;
   if (q != nullptr) {
-    if (q_out != q && overlap(q_out, bytes, q, bytes)) return ATTN_ERR_ALIAS;
-    if (overlap(q_out, bytes, k, bytes) || overlap(k_out, bytes, q, bytes) ||
-        overlap(q_out, bytes, k_out, bytes))
+    if (q_out != q && overlap(q_out, qb, q, qb)) return ATTN_ERR_ALIAS;
+    if (overlap(q_out, qb, k, kb) || overlap(k_out, kb, q, qb) || overlap(q_out, qb, k_out, kb))
       return ATTN_ERR_ALIAS;
   }
-  hipError_t e = attn::launch_qknorm_rope(q, k, q_out, k_out, cos_tab, sin_tab, B, H, T, d, eps,
-                                          dtype, (hipStream_t)stream);
+  hipError_t e = attn::launch_qknorm_rope(q, k, q_out, k_out, cos_tab, sin_tab, dm, eps, dtype,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos_tab,
+                     const float* sin_tab, int B, int H, int T, int d, float eps, int dtype,
+                     void* stream) {
+  return attn_qknorm_rope_ex(q, k, q_out, k_out, cos_tab, sin_tab, B, H, H, T, d,
+                             ATTN_LAYOUT_BHTD, eps, dtype, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                int H_kv, int T, int d, int layout, int window, int causal, int dtype,
+                void* stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (dtype == ATTN_BF16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_dims(B, H, H_kv, T, d, layout, &dm, &n_q, &n_kv)) return rc;
+  if (causal != 0 && causal != 1) return ATTN_ERR_WINDOW;
+  if (window < -1 || (causal == 0 && window != -1)) return ATTN_ERR_WINDOW;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_ALIGN;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
+  const int64_t qb = n_q * elem_bytes(dtype), kb = n_kv * elem_bytes(dtype);
+  if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb))
+    return ATTN_ERR_ALIAS;
+  const int64_t bh = (int64_t)B * H;
+  if (lse != nullptr) {
+    const int64_t lbytes = bh * T * 4;
+    if (overlap(lse, lbytes, q, qb) || overlap(lse, lbytes, k, kb) ||
+        overlap(lse, lbytes, v, kb) || overlap(lse, lbytes, out, qb))
+      return ATTN_ERR_ALIAS;
+  }
+  if (dtype == ATTN_BF16 && !slab_fits(dm)) return ATTN_ERR_SHAPE;
+  const int64_t tiles = (dtype == ATTN_BF16) ? (T + 127) / 128 : (T + 63) / 64;
+  if (bh * tiles > kMaxGrid) return ATTN_ERR_SHAPE;
+  hipError_t e;
+  if (dtype == ATTN_BF16)
+    e = attn::launch_attn_fwd_bf16(q, k, v, out, lse, dm, window, causal, (hipStream_t)stream);
+  else
+    e = attn::launch_attn_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)out,
+                                  lse, dm, window, causal, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
              int T, int d, int window, int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
-  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
-  if (dtype == ATTN_BF16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  int64_t n = 0;
-  if (int rc = check_shape(B, H, T, d, &n)) return rc;
-  if (causal != 0 && causal != 1) return ATTN_ERR_WINDOW;
-  if (window < -1 || (causal == 0 && window != -1)) return ATTN_ERR_WINDOW;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_ALIGN;
-  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
-  const int64_t bytes = n * elem_bytes(dtype);
-  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) ||
-      overlap(out, bytes, v, bytes))
-    return ATTN_ERR_ALIAS;
-  const int64_t bh = (int64_t)B * H;
-  if (lse != nullptr) {
-    const int64_t lbytes = bh * T * 4;
-    if (overlap(lse, lbytes, q, bytes) || overlap(lse, lbytes, k, bytes) ||
-        overlap(lse, lbytes, v, bytes) || overlap(lse, lbytes, out, bytes))
-      return ATTN_ERR_ALIAS;
-  }
-  // One head's [T][d] slab (plus a query block of padding rows) must stay below 2^31 bytes: the
-  // bf16 kernel addresses it through 32-bit buffer offsets.
-  if (dtype == ATTN_BF16 && ((int64_t)T + 128) * d * 2 >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
-  const int64_t tiles = (dtype == ATTN_BF16) ? (T + 127) / 128 : (T + 63) / 64;
-  if (bh * tiles > kMaxGrid) return ATTN_ERR_SHAPE;
-  hipError_t e;
-  if (dtype == ATTN_BF16)
-    e = attn::launch_attn_fwd_bf16(q, k, v, out, lse, B, H, T, d, window, causal,
-                                   (hipStream_t)stream);
-  else
-    e = attn::launch_attn_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)out,
-                                  lse, B, H, T, d, window, causal, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return attn_fwd_ex(q, k, v, out, lse, B, H, H, T, d, ATTN_LAYOUT_BHTD, window, causal, dtype,
+                     stream);
 }
 
 namespace {
 
-// Checks shared by attn_fwd_qnorm and attn_fwd_qknorm (k here is the tensor the attention
+// Checks shared by attn_fwd_qnorm_ex and attn_fwd_qknorm_ex (k here is the tensor the attention
 // kernel reads as keys).
 int check_qnorm_args(const void* q, const void* k, const void* v, const void* out,
                      const float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
-                     int T, int d, float eps, int window, int causal, int dtype, int64_t* n) {
+                     int H_kv, int T, int d, int layout, float eps, int window, int causal,
+                     int dtype, attn::Dims* dm, int64_t* n_q, int64_t* n_kv) {
   if (!q || !k || !v || !out || !cos_tab || !sin_tab) return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (int rc = check_shape(B, H, T, d, n)) return rc;
+  if (int rc = check_dims(B, H, H_kv, T, d, layout, dm, n_q, n_kv)) return rc;
   if (causal != 0 && causal != 1) return ATTN_ERR_WINDOW;
   if (window < -1 || (causal == 0 && window != -1)) return ATTN_ERR_WINDOW;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ATTN_ERR_ARG;
@@ -172,61 +208,75 @@ int check_qnorm_args(const void* q, const void* k, const void* v, const void* ou
       !aligned16(sin_tab))
     return ATTN_ERR_ALIGN;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
-  const int64_t bytes = *n * 2;
-  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) ||
-      overlap(out, bytes, v, bytes))
+  const int64_t qb = *n_q * 2, kb = *n_kv * 2;
+  if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb))
     return ATTN_ERR_ALIAS;
   const int64_t bh = (int64_t)B * H;
   if (lse != nullptr) {
     const int64_t lbytes = bh * T * 4;
-    if (overlap(lse, lbytes, q, bytes) || overlap(lse, lbytes, k, bytes) ||
-        overlap(lse, lbytes, v, bytes) || overlap(lse, lbytes, out, bytes))
+    if (overlap(lse, lbytes, q, qb) || overlap(lse, lbytes, k, kb) ||
+        overlap(lse, lbytes, v, kb) || overlap(lse, lbytes, out, qb))
       return ATTN_ERR_ALIAS;
   }
-  // 32-bit buffer offsets: one head's slab plus a query block, and the rotation tables.
-  if (((int64_t)T + 128) * d * 2 >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
+  if (!slab_fits(*dm)) return ATTN_ERR_SHAPE;
   if (bh * ((T + 127) / 128) > kMaxGrid) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
 }  // namespace
 
+int attn_fwd_qnorm_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                      const float* cos_tab, const float* sin_tab, int B, int H, int H_kv, int T,
+                      int d, int layout, float eps, int window, int causal, int dtype,
+                      void* stream) {
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_qnorm_args(q, k, v, out, lse, cos_tab, sin_tab, B, H, H_kv, T, d, layout,
+                                eps, window, causal, dtype, &dm, &n_q, &n_kv))
+    return rc;
+  const hipError_t e = attn::launch_attn_fwd_bf16_qknorm(q, k, v, out, lse, cos_tab, sin_tab, eps,
+                                                         dm, window, causal, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_fwd_qnorm(const void* q, const void* k, const void* v, void* out, float* lse,
                    const float* cos_tab, const float* sin_tab, int B, int H, int T, int d,
                    float eps, int window, int causal, int dtype, void* stream) {
-  int64_t n = 0;
-  if (int rc = check_qnorm_args(q, k, v, out, lse, cos_tab, sin_tab, B, H, T, d, eps, window,
-                                causal, dtype, &n))
+  return attn_fwd_qnorm_ex(q, k, v, out, lse, cos_tab, sin_tab, B, H, H, T, d, ATTN_LAYOUT_BHTD,
+                           eps, window, causal, dtype, stream);
+}
+
+int attn_fwd_qknorm_ex(const void* q, const void* k, const void* v, void* k_work, void* out,
+                       float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
+                       int H_kv, int T, int d, int layout, float eps, int window, int causal,
+                       int dtype, void* stream) {
+  if (!k_work) return ATTN_ERR_NULL;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_qnorm_args(q, k_work, v, out, lse, cos_tab, sin_tab, B, H, H_kv, T, d,
+                                layout, eps, window, causal, dtype, &dm, &n_q, &n_kv))
     return rc;
-  const hipError_t e = attn::launch_attn_fwd_bf16_qknorm(q, k, v, out, lse, cos_tab, sin_tab, eps,
-                                                         B, H, T, d, window, causal,
-                                                         (hipStream_t)stream);
+  if (!k) return ATTN_ERR_NULL;
+  if (!aligned16(k)) return ATTN_ERR_ALIGN;
+  if (2 * (int64_t)B * H > 0x7fffffff) return ATTN_ERR_SHAPE;
+  const int64_t qb = n_q * 2, kb = n_kv * 2;
+  if (k_work != k && overlap(k_work, kb, k, kb)) return ATTN_ERR_ALIAS;
+  if (overlap(k_work, kb, q, qb) || overlap(k_work, kb, v, kb) || overlap(out, qb, k, kb))
+    return ATTN_ERR_ALIAS;
+  if (lse != nullptr && overlap(lse, (int64_t)B * H * T * 4, k, kb)) return ATTN_ERR_ALIAS;
+  hipError_t e = attn::launch_qknorm_rope(nullptr, k, nullptr, k_work, cos_tab, sin_tab, dm, eps,
+                                          ATTN_BF16, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = attn::launch_attn_fwd_bf16_qknorm(q, k_work, v, out, lse, cos_tab, sin_tab, eps, dm,
+                                          window, causal, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, void* out,
                     float* lse, const float* cos_tab, const float* sin_tab, int B, int H, int T,
                     int d, float eps, int window, int causal, int dtype, void* stream) {
-  if (!k_work) return ATTN_ERR_NULL;
-  int64_t n = 0;
-  if (int rc = check_qnorm_args(q, k_work, v, out, lse, cos_tab, sin_tab, B, H, T, d, eps,
-                                window, causal, dtype, &n))
-    return rc;
-  if (!k) return ATTN_ERR_NULL;
-  if (!aligned16(k)) return ATTN_ERR_ALIGN;
-  if (2 * (int64_t)B * H > 0x7fffffff) return ATTN_ERR_SHAPE;
-  const int64_t bytes = n * 2;
-  if (k_work != k && overlap(k_work, bytes, k, bytes)) return ATTN_ERR_ALIAS;
-  if (overlap(k_work, bytes, q, bytes) || overlap(k_work, bytes, v, bytes) ||
-      overlap(out, bytes, k, bytes))
-    return ATTN_ERR_ALIAS;
-  if (lse != nullptr && overlap(lse, (int64_t)B * H * T * 4, k, bytes)) return ATTN_ERR_ALIAS;
-  hipError_t e = attn::launch_qknorm_rope(nullptr, k, nullptr, k_work, cos_tab, sin_tab, B, H, T,
-                                          d, eps, ATTN_BF16, (hipStream_t)stream);
-  if (e == hipSuccess)
-    e = attn::launch_attn_fwd_bf16_qknorm(q, k_work, v, out, lse, cos_tab, sin_tab, eps, B, H, T,
-                                          d, window, causal, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return attn_fwd_qknorm_ex(q, k, v, k_work, out, lse, cos_tab, sin_tab, B, H, H, T, d,
+                            ATTN_LAYOUT_BHTD, eps, window, causal, dtype, stream);
 }
 
 }  // extern "C"

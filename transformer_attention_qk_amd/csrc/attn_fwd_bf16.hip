@@ -195,6 +195,7 @@ struct WaveTile {
   using C = FwdCfg<D>;
   static constexpr bool causal = MODE != kNonCausal;
   int T, window, lane, l32, hi, wave;
+  int q_rs;  // bytes between consecutive q (and out) rows
   float scale_log2;
   // lane-constant LDS addressing. K (A operand of S^T): row 32 kb + l32, logical chunk
   // 2 s + hi. V (A operand of O^T via the transposing read): lane (4a + b) of each 16-lane group
@@ -207,8 +208,9 @@ struct WaveTile {
   f32x16 oacc[C::DB];
   float m_run, l_run0, l_run1;  // running max (base-2 units) and this lane's two partial sums
 
-  __device__ __forceinline__ void init(int T_, int window_, float scale_log2_, int tid) {
+  __device__ __forceinline__ void init(int T_, int window_, float scale_log2_, int tid, int q_rs_) {
     T = T_;
+    q_rs = q_rs_;
     window = window_;
     scale_log2 = scale_log2_;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,7 +331,7 @@ struct WaveTile {
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
       xf[s] = __builtin_bit_cast(
-          bf16x8, buffer_load16(rq, (uint32_t)(q_row(q0) * C::ROW_BYTES + 32 * s + 16 * hi)));
+          bf16x8, buffer_load16(rq, (uint32_t)(q_row(q0) * q_rs + 32 * s + 16 * hi)));
   }
   __device__ __forceinline__ void load_q_lds(const char* qbuf, bf16x8 (&xf)[C::KSTEPS]) const {
     const int ln = lane_now();
@@ -559,7 +561,7 @@ struct WaveTile {
     const float l_tot = pair_sum(l_run0 + l_run1);
     if (qi < T) {
       const float inv = 1.0f / l_tot;
-      bf16* orow = O + hoff + (int64_t)qi * D;
+      bf16* orow = O + hoff + (int64_t)qi * (q_rs / 2);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -595,18 +597,20 @@ template <int D, int MODE, bool QKN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
-    const float* __restrict__ sin_tab, float eps, int BH, int T, int window_arg,
+    const float* __restrict__ sin_tab, float eps, Geometry geo, int BH, int T, int window_arg,
     float scale_log2, int nqt) {
   using C = FwdCfg<D>;
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::STREAM_LDS];
   const int tid = threadIdx.x;
+  const int q_rs = geo.q.t * 2, kv_rs = geo.kv.t * 2;  // row strides in bytes
   WaveTile<D, MODE, QKN> w;
-  w.init(T, window, scale_log2, tid);
+  w.init(T, window, scale_log2, tid, q_rs);
   const int P = (int)gridDim.x;
   const int g = (int)blockIdx.x;
   const int n_items = BH * nqt;
-  const int slab = T * C::ROW_BYTES;  // bytes of one head's [T][d] slab (< 2^31, checked)
+  // bytes spanned by one head's T rows (< 2^31, checked); rows past T read as zero
+  const int q_slab = T * q_rs, kv_slab = T * kv_rs;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   const char* qbuf = smem + C::NSTAGE * 2 * C::TILE_BYTES;
 
@@ -626,19 +630,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   for (int u = 0; u < C::LPT; ++u) {
     const unsigned p = (unsigned)((w.wave * C::LPT + u) * 64 + w.lane);
     const unsigned r = p / C::CH, pc = p % C::CH;
-    kofs[u] = r * C::ROW_BYTES + 16 * (pc ^ swz_k<D>((int)r));
-    vofs[u] = r * C::ROW_BYTES + 16 * (pc ^ swz_v<D>((int)r));
+    kofs[u] = r * kv_rs + 16 * (pc ^ swz_k<D>((int)r));
+    vofs[u] = r * kv_rs + 16 * (pc ^ swz_v<D>((int)r));
   }
   // Direct loads of the Q block of an item into the Q buffer (K layout).
   auto dma_q = [&](int bh, int q0) {
-    const u32x4 rq = head_rsrc_words(Q + (int64_t)bh * T * D, slab);
+    const u32x4 rq = head_rsrc_words(Q + geo.q_head(bh), q_slab);
     const uint32_t qb_ = lds0 + C::NSTAGE * 2 * C::TILE_BYTES;
 #pragma unroll
     for (int u = 0; u < C::DMA_PER_Q; ++u) {
       const unsigned run = (unsigned)(w.wave * C::DMA_PER_Q + u);
       const unsigned p = run * 64 + (unsigned)w.lane;
       const unsigned r = p / C::CH, pc = p % C::CH;
-      dma16(rq, qb_ + run * 1024, ((unsigned)q0 + r) * C::ROW_BYTES + 16 * (pc ^ swz_k<D>((int)r)));
+      dma16(rq, qb_ + run * 1024, ((unsigned)q0 + r) * q_rs + 16 * (pc ^ swz_k<D>((int)r)));
     }
   };
 
@@ -672,15 +676,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   auto seek = [&](int rank) {
     int bh_, q0_;
     decode(rank, bh_, q0_, pt, pte);
-    const int64_t hoff = (int64_t)bh_ * T * D;
-    prk = head_rsrc_words(K + hoff, slab);
-    prv = head_rsrc_words(V + hoff, slab);
+    const int64_t hoff = geo.kv_head(bh_);
+    prk = head_rsrc_words(K + hoff, kv_slab);
+    prv = head_rsrc_words(V + hoff, kv_slab);
   };
   seek(rank_of(0));  // g < P <= n_items
   auto issue_next = [&]() {
     const uint32_t kb_ = lds0 + st_issue * (2 * C::TILE_BYTES) + w.wave * (C::LPT * 1024);
     const uint32_t vb_ = kb_ + C::TILE_BYTES;
-    const uint32_t base = pvalid ? (uint32_t)(pt * C::TILE_BYTES) : kOutOfRange;
+    const uint32_t base = pvalid ? (uint32_t)(pt * C::BN * kv_rs) : kOutOfRange;
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
       dma16(prk, kb_ + u * 1024, base + kofs[u]);
@@ -708,7 +712,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   typename WaveTile<D, MODE, QKN>::Rope rope;
   {
     bf16x8 xf[C::KSTEPS];
-    w.load_q_global(head_rsrc(Q + (int64_t)bh * T * D, slab), q0, xf);
+    w.load_q_global(head_rsrc(Q + geo.q_head(bh), q_slab), q0, xf);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     w.rope_from_lds(smem + (C::NSTAGE - 1) * (2 * C::TILE_BYTES), rope);
@@ -807,7 +811,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     // and the wait for them. The next item's Q fragments are formed first: no store is then in
     // flight between the rotation factors' loads and their use.
     if (!more) {
-      w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
+      w.store(O, LSE, geo.q_head(bh), (int64_t)bh * T);
       // The stream's last loads (out of range, writing zeros) land before the workgroup's LDS
       // is released.
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -822,7 +826,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       w.load_q_lds(qbuf, xf);
       w.set_q(xf, rope, nq0, eps);
     }
-    w.store(O, LSE, (int64_t)bh * T * D, (int64_t)bh * T);
+    w.store(O, LSE, geo.q_head(bh), (int64_t)bh * T);
     ++k;
     bh = nbh;
     q0 = nq0;
@@ -842,27 +846,27 @@ template <int D, int MODE, bool QKN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
-    const float* __restrict__ sin_tab, float eps, int BH, int T, int window_arg,
+    const float* __restrict__ sin_tab, float eps, Geometry geo, int BH, int T, int window_arg,
     float scale_log2, int nqt) {
   using C = FwdCfg<D>;
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::TILE_LDS];
   const int tid = threadIdx.x;
+  const int q_rs = geo.q.t * 2, kv_rs = geo.kv.t * 2;  // row strides in bytes
   WaveTile<D, MODE, QKN> w;
-  w.init(T, window, scale_log2, tid);
+  w.init(T, window, scale_log2, tid, q_rs);
   const int bh = (int)(blockIdx.x % BH);
   const int q0 = (nqt - 1 - (int)(blockIdx.x / BH)) * C::BM;  // heaviest query block first
-  const int64_t hoff = (int64_t)bh * T * D;
-  const int slab = T * C::ROW_BYTES;
-  const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + hoff, slab);
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + hoff, slab);
+  const int64_t hoff = geo.q_head(bh), kvoff = geo.kv_head(bh);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + kvoff, T * kv_rs);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kvoff, T * kv_rs);
   int tb, te;
   item_tiles<D, MODE>(q0, T, window, tb, te);
   w.set_item(q0);
   {
     bf16x8 xf[C::KSTEPS];
     typename WaveTile<D, MODE, QKN>::Rope rope;
-    w.load_q_global(head_rsrc(Q + hoff, slab), q0, xf);
+    w.load_q_global(head_rsrc(Q + hoff, T * q_rs), q0, xf);
     w.load_rope(q0, cos_tab, sin_tab, rope);
     w.set_q(xf, rope, q0, eps);
   }
@@ -872,7 +876,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
     for (int u = 0; u < C::LPT; ++u) {
       const int e = tid + 256 * u;
       const uint32_t off =
-          needed ? (uint32_t)((t * C::BN + e / C::CH) * C::ROW_BYTES + 16 * (e % C::CH)) : kOutOfRange;
+          needed ? (uint32_t)((t * C::BN + e / C::CH) * kv_rs + 16 * (e % C::CH)) : kOutOfRange;
       st[u] = buffer_load16(r, off);
     }
   };
@@ -935,6 +939,7 @@ struct Bf16Args {
   const float *cos_tab, *sin_tab;
   float eps;
   int B, H, T, window;
+  Geometry geo;
 };
 
 template <int D, int MODE, bool QKN>
@@ -950,11 +955,11 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
     const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
     hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN>), dim3(grid), dim3(256), 0, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse,
-                       a.cos_tab, a.sin_tab, a.eps, BH, a.T, a.window, scale_log2, nqt);
+                       a.cos_tab, a.sin_tab, a.eps, a.geo, BH, a.T, a.window, scale_log2, nqt);
   } else {
     hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE, QKN>), dim3((unsigned)n_items), dim3(256), 0,
                        stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out,
-                       a.lse, a.cos_tab, a.sin_tab, a.eps, BH, a.T, a.window, scale_log2, nqt);
+                       a.lse, a.cos_tab, a.sin_tab, a.eps, a.geo, BH, a.T, a.window, scale_log2, nqt);
   }
   return hipGetLastError();
 }
@@ -982,18 +987,19 @@ static hipError_t launch_bf16(const Bf16Args& a, int d, int causal, hipStream_t 
 }
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
-                                int B, int H, int T, int d, int window, int causal,
-                                hipStream_t stream) {
-  const Bf16Args a{q, k, v, out, lse, nullptr, nullptr, 0.f, B, H, T, window};
-  return launch_bf16<false>(a, d, causal, stream);
+                                const Dims& dm, int window, int causal, hipStream_t stream) {
+  const Bf16Args a{q, k, v, out, lse, nullptr, nullptr, 0.f, dm.B, dm.H, dm.T, window,
+                   make_geometry(dm)};
+  return launch_bf16<false>(a, dm.d, causal, stream);
 }
 
 hipError_t launch_attn_fwd_bf16_qknorm(const void* q, const void* k, const void* v, void* out,
                                        float* lse, const float* cos_tab, const float* sin_tab,
-                                       float eps, int B, int H, int T, int d, int window,
-                                       int causal, hipStream_t stream) {
-  const Bf16Args a{q, k, v, out, lse, cos_tab, sin_tab, eps, B, H, T, window};
-  return launch_bf16<true>(a, d, causal, stream);
+                                       float eps, const Dims& dm, int window, int causal,
+                                       hipStream_t stream) {
+  const Bf16Args a{q, k, v, out, lse, cos_tab, sin_tab, eps, dm.B, dm.H, dm.T, window,
+                   make_geometry(dm)};
+  return launch_bf16<true>(a, dm.d, causal, stream);
 }
 
 }  // namespace attn

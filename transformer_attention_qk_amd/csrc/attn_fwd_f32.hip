@@ -23,21 +23,22 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
                                                           const float* __restrict__ K,
                                                           const float* __restrict__ V,
                                                           float* __restrict__ O,
-                                                          float* __restrict__ LSE, int BH, int T,
-                                                          int window, int causal, float scale_log2,
-                                                          int nqb) {
+                                                          float* __restrict__ LSE, Geometry geo,
+                                                          int BH, int T, int window, int causal,
+                                                          float scale_log2, int nqb) {
   constexpr int BN = 32;
   __shared__ float ks[BN * D];
   __shared__ float vs[BN * D];
   const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // heaviest query blocks first
   const int bh = (int)(blockIdx.x % BH);
-  const int64_t hoff = (int64_t)bh * T * D;
+  const int64_t hoff = geo.q_head(bh), kvoff = geo.kv_head(bh);
+  const int qs = geo.q.t, ks_ = geo.kv.t;  // row strides in elements
   const int q0 = qb * 64;
   const int i = q0 + (int)threadIdx.x;
 
   float qr[D];
 #pragma unroll
-  for (int c = 0; c < D; ++c) qr[c] = (i < T) ? Q[hoff + (int64_t)i * D + c] : 0.f;
+  for (int c = 0; c < D; ++c) qr[c] = (i < T) ? Q[hoff + (int64_t)i * qs + c] : 0.f;
   float o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) o[c] = 0.f;
@@ -53,8 +54,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
     for (int e = threadIdx.x; e < BN * D; e += 64) {
       const int j = kt + e / D;
       const bool in = j < T;
-      ks[e] = in ? K[hoff + (int64_t)j * D + e % D] : 0.f;
-      vs[e] = in ? V[hoff + (int64_t)j * D + e % D] : 0.f;
+      ks[e] = in ? K[kvoff + (int64_t)j * ks_ + e % D] : 0.f;
+      vs[e] = in ? V[kvoff + (int64_t)j * ks_ + e % D] : 0.f;
     }
     __syncthreads();
     const int jn = min(BN, hi - kt);
@@ -82,22 +83,23 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restric
   if (i < T) {
     const float inv = 1.0f / l;
 #pragma unroll
-    for (int c = 0; c < D; ++c) O[hoff + (int64_t)i * D + c] = o[c] * inv;
+    for (int c = 0; c < D; ++c) O[hoff + (int64_t)i * qs + c] = o[c] * inv;
     if (LSE) LSE[(int64_t)bh * T + i] = (m + log2f(l)) * kLn2;
   }
 }
 
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
-                               float* lse, int B, int H, int T, int d, int window, int causal,
+                               float* lse, const Dims& dm, int window, int causal,
                                hipStream_t stream) {
-  const int BH = B * H;
+  const int BH = dm.B * dm.H, T = dm.T, d = dm.d;
+  const Geometry geo = make_geometry(dm);
   const int nqb = (T + 63) / 64;
   const unsigned grid = (unsigned)((int64_t)BH * nqb);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
 #define ATTN_F32_CASE(DD)                                                                       \
   if (d == DD) {                                                                                \
     hipLaunchKernelGGL(attn_fwd_f32_kernel<DD>, dim3(grid), dim3(64), 0, stream, q, k, v, out, \
-                       lse, BH, T, window, causal, scale_log2, nqb);                           \
+                       lse, geo, BH, T, window, causal, scale_log2, nqb);                      \
     return hipGetLastError();                                                                   \
   }
   ATTN_F32_CASE(16)

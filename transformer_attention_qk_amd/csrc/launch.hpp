@@ -6,29 +6,68 @@
 
 namespace attn {
 
+// Shape of one call: q and out are [B, H, T, d], k and v [B, H_kv, T, d] (H_kv divides H), all
+// stored as [B][H][T][d] (layout 0) or [B][T][H][d] (layout 1).
+struct Dims {
+  int B, H, H_kv, T, d, layout;
+};
+
+// Where the rows of one (batch, head) live: element offset b * b + h * h + t * t of a [B, H, T, d]
+// tensor stored as [B][H][T][d] or as [B][T][H][d]; q and out share one, k and v another (k and
+// v have H / group heads: grouped-query attention maps q head h to kv head h / group).
+struct Strides {
+  int64_t b, h;
+  int t;
+};
+struct Geometry {
+  Strides q, kv;
+  int H, group;
+  __host__ __device__ __forceinline__ int64_t q_head(int bh) const {
+    return (int64_t)(bh / H) * q.b + (int64_t)(bh % H) * q.h;
+  }
+  __host__ __device__ __forceinline__ int64_t kv_head(int bh) const {
+    return (int64_t)(bh / H) * kv.b + (int64_t)((bh % H) / group) * kv.h;
+  }
+};
+
+inline Geometry make_geometry(const Dims& dm) {
+  Geometry g;
+  const int64_t d = dm.d;
+  if (dm.layout == 0) {  // [B][H][T][d]
+    g.q = Strides{(int64_t)dm.H * dm.T * d, (int64_t)dm.T * d, (int)d};
+    g.kv = Strides{(int64_t)dm.H_kv * dm.T * d, (int64_t)dm.T * d, (int)d};
+  } else {  // [B][T][H][d]
+    g.q = Strides{(int64_t)dm.T * dm.H * d, d, (int)(dm.H * d)};
+    g.kv = Strides{(int64_t)dm.T * dm.H_kv * d, d, (int)(dm.H_kv * d)};
+  }
+  g.H = dm.H;
+  g.group = dm.H / dm.H_kv;
+  return g;
+}
+
+
 hipError_t launch_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base,
                              hipStream_t stream);
 
 // dtype: 0 = bf16, 1 = f32. d in {16, 32, 64, 128}. q == nullptr: k rows only (q_out unused).
 hipError_t launch_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
-                              const float* cos_tab, const float* sin_tab, int B, int H, int T,
-                              int d, float eps, int dtype, hipStream_t stream);
+                              const float* cos_tab, const float* sin_tab, const Dims& dm,
+                              float eps, int dtype, hipStream_t stream);
 
 // bf16 attention on MFMA. d in {32, 64, 128}.
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
-                                int B, int H, int T, int d, int window, int causal,
-                                hipStream_t stream);
+                                const Dims& dm, int window, int causal, hipStream_t stream);
 
 // bf16 attention on MFMA whose Q rows are RMS-normalised and rotated inside the kernel (k must
 // already be normalised and rotated). d in {32, 64, 128}.
 hipError_t launch_attn_fwd_bf16_qknorm(const void* q, const void* k, const void* v, void* out,
                                        float* lse, const float* cos_tab, const float* sin_tab,
-                                       float eps, int B, int H, int T, int d, int window,
-                                       int causal, hipStream_t stream);
+                                       float eps, const Dims& dm, int window, int causal,
+                                       hipStream_t stream);
 
 // fp32 attention. d in {16, 32, 64, 128}.
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
-                               float* lse, int B, int H, int T, int d, int window, int causal,
+                               float* lse, const Dims& dm, int window, int causal,
                                hipStream_t stream);
 
 }  // namespace attn

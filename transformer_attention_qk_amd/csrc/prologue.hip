@@ -78,7 +78,8 @@ template <typename Elem>
 constexpr int kE = (sizeof(Elem) == 2) ? 8 : 4;
 
 // Rows are grouped by position: a block handles TPB positions t of R heads, where the heads are
-// q's B*H heads (when q is given) followed by k's. A row is handled by L = d / E lanes, lane i
+// q's B*H heads (when q is given) followed by k's B*H_kv heads; a head's rows start at
+// b * stride.b + h * stride.h and are stride.t elements apart (either storage order). A row is handled by L = d / E lanes, lane i
 // holding the row's i-th 16-byte chunk, so a wave's loads and stores cover whole rows. The
 // element j < d/2 and its rotation partner j + d/2 sit in lanes i and i ^ (L/2), which swap
 // their chunks with one xor shuffle per 32-bit word; the sum of squares crosses the L lanes by
@@ -86,13 +87,12 @@ constexpr int kE = (sizeof(Elem) == 2) ? 8 : 4;
 template <typename Elem, int D, int R>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const Elem* __restrict__ q, const Elem* __restrict__ k, Elem* q_out, Elem* k_out,
-    const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, int heads_q,
-    int heads, int T, int t_blocks, float eps) {
+    const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, Strides sq, Strides sk,
+    int H, int H_kv, int heads_q, int heads, int T, int t_blocks, float eps) {
   constexpr int E = kE<Elem>;
   constexpr int HALF = D / 2;
   constexpr int L = D / E;      // lanes per row (2 .. 32)
   constexpr int TPB = 256 / L;  // positions per block
-  constexpr int W = E * sizeof(Elem) / 4;  // 32-bit words per chunk
   const int tb = (int)(blockIdx.x % (unsigned)t_blocks);
   const int h0 = (int)(blockIdx.x / (unsigned)t_blocks) * R;
   const int t = tb * TPB + (int)threadIdx.x / L;
@@ -112,14 +112,20 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     Vec<float, 4>::load(ct + i, c + i);
     Vec<float, 4>::load(st + i, s + i);
   }
+  // Element offset of row t of head h (block-uniform apart from t).
+  auto row = [&](int h) -> int64_t {
+    if (h < heads_q) return (int64_t)(h / H) * sq.b + (int64_t)(h % H) * sq.h + (int64_t)t * sq.t;
+    const int hk = h - heads_q;
+    return (int64_t)(hk / H_kv) * sk.b + (int64_t)(hk % H_kv) * sk.h + (int64_t)t * sk.t;
+  };
   u32x4 raw[R];
+  int64_t off[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = h0 + r;  // block-uniform
     if (h < total) {
-      const Elem* src = (h < heads_q ? q + (int64_t)h * T * D : k + (int64_t)(h - heads_q) * T * D) +
-                        (int64_t)t * D + sub * E;
-      raw[r] = *reinterpret_cast<const u32x4*>(src);
+      off[r] = row(h) + sub * E;
+      raw[r] = *reinterpret_cast<const u32x4*>((h < heads_q ? q : k) + off[r]);
     }
   }
 #pragma unroll
@@ -145,36 +151,35 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
       // first half: x_j cos + x_{j+h} sin; second half: -x_j sin + x_{j+h} cos
       y[i] = first ? fmaf(a, c[i], b * s[i]) : fmaf(a, c[i], -(b * s[i]));
     }
-    Elem* dst = (h < heads_q ? q_out + (int64_t)h * T * D : k_out + (int64_t)(h - heads_q) * T * D) +
-                (int64_t)t * D + sub * E;
-    Vec<Elem, E>::store(dst, y);
+    Vec<Elem, E>::store((h < heads_q ? q_out : k_out) + off[r], y);
   }
 }
 
 template <typename Elem, int D>
 static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out, void* k_out,
-                                       const float* cos_tab, const float* sin_tab, int B, int H,
-                                       int T, float eps, hipStream_t stream) {
+                                       const float* cos_tab, const float* sin_tab, const Dims& dm,
+                                       float eps, hipStream_t stream) {
   constexpr int R = 2;  // rows per lane
   constexpr int L = D / kE<Elem>;
   constexpr int TPB = 256 / L;
-  const int heads = B * H;
-  const int heads_q = (q != nullptr) ? heads : 0;
+  const int T = dm.T;
+  const Geometry geo = make_geometry(dm);
+  const int heads = dm.B * dm.H_kv;
+  const int heads_q = (q != nullptr) ? dm.B * dm.H : 0;
   const int t_blocks = (T + TPB - 1) / TPB;
   const int64_t grid = (int64_t)t_blocks * ((heads_q + heads + R - 1) / R);
   hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
                      (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, cos_tab, sin_tab,
-                     heads_q, heads, T, t_blocks, eps);
+                     geo.q, geo.kv, dm.H, dm.H_kv, heads_q, heads, T, t_blocks, eps);
   return hipGetLastError();
 }
 
 hipError_t launch_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
-                              const float* cos_tab, const float* sin_tab, int B, int H, int T,
-                              int d, float eps, int dtype, hipStream_t stream) {
-#define ATTN_QKN_CASE(ELEM, DD)                                                              \
-  if (d == DD)                                                                               \
-    return launch_qknorm_rope_t<ELEM, DD>(q, k, q_out, k_out, cos_tab, sin_tab, B, H, T, eps, \
-                                          stream);
+                              const float* cos_tab, const float* sin_tab, const Dims& dm,
+                              float eps, int dtype, hipStream_t stream) {
+  const int d = dm.d;
+#define ATTN_QKN_CASE(ELEM, DD) \
+  if (d == DD) return launch_qknorm_rope_t<ELEM, DD>(q, k, q_out, k_out, cos_tab, sin_tab, dm, eps, stream);
   if (dtype == 0) {
     ATTN_QKN_CASE(bf16, 16)
     ATTN_QKN_CASE(bf16, 32)

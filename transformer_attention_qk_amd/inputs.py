@@ -51,11 +51,21 @@ WORKLOADS: tuple[Workload, ...] = (
 
 HEADLINE = 2  # index of the ANDREA-120M SSSL stack
 
+# The default model of the autoresearch train.py listing ("Подробный технический разбор
+# реализации Autoresearch", habr.com: DEPTH 8, ASPECT_RATIO 64 so d_model 512, HEAD_DIM 128 so 4
+# heads, n_kv_head = n_head, MAX_SEQ_LEN 2048, DEVICE_BATCH_SIZE 128, WINDOW_PATTERN "SSSL").
+# Its attention runs on q, k, v in the projections' [B][T][H][d] order; make_qkv draws them in
+# [B, H, T, d] order like every workload, and callers transpose.
+MODEL_DEFAULT = Workload("autoresearch_default", B=128, H=4, T=2048, d=128, dtype="bf16",
+                         pattern="SSSL", n_layer=8)
+MODEL_DEFAULT_INDEX = len(WORKLOADS)  # make_qkv index (and seed index) of MODEL_DEFAULT
+_ALL = WORKLOADS + (MODEL_DEFAULT,)
+
 
 def workload(name_or_index) -> Workload:
     if isinstance(name_or_index, int):
-        return WORKLOADS[name_or_index]
-    for w in WORKLOADS:
+        return _ALL[name_or_index]
+    for w in _ALL:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)
@@ -72,7 +82,7 @@ def make_qkv(index: int, layer: int = 0, shape: tuple[int, int, int, int] | None
     Drawn in fp32 in the order q, k, v from a CPU generator, then rounded to bf16 (round to
     nearest even) for bf16 workloads. ``shape`` overrides (B, H, T, d) for reduced test sizes.
     """
-    w = WORKLOADS[index]
+    w = _ALL[index]
     B, H, T, d = shape if shape is not None else (w.B, w.H, w.T, w.d)
     g = torch.Generator(device="cpu").manual_seed(seed_for(index, layer))
     q = torch.randn((B, H, T, d), generator=g, dtype=torch.float32)

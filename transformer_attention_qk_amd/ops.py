@@ -14,6 +14,7 @@ import torch
 from . import _lib
 
 _DTYPES = {torch.bfloat16: _lib.ATTN_BF16, torch.float32: _lib.ATTN_F32}
+_LAYOUTS = {"bhtd": _lib.ATTN_LAYOUT_BHTD, "bthd": _lib.ATTN_LAYOUT_BTHD}
 
 
 def _stream_handle() -> int:
@@ -37,6 +38,44 @@ def _require(t: torch.Tensor, name: str, shape=None, dtype=None) -> None:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _geometry(q: torch.Tensor | None, k: torch.Tensor, layout: str):
+    """(B, H, H_kv, T, d) of q and k stored as [B, H, T, d] ("bhtd") or [B, T, H, d] ("bthd");
+    k (and v) may have fewer heads than q (grouped-query attention)."""
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}, got {layout!r}")
+    if k.dim() != 4 or (q is not None and q.dim() != 4):
+        raise ValueError("q and k must be 4-d tensors")
+    if layout == "bhtd":
+        B, H_kv, T, d = k.shape
+        H = q.shape[1] if q is not None else H_kv
+    else:
+        B, T, H_kv, d = k.shape
+        H = q.shape[2] if q is not None else H_kv
+    if q is not None:
+        want = (B, H, T, d) if layout == "bhtd" else (B, T, H, d)
+        if tuple(q.shape) != want:
+            raise ValueError(f"q has shape {tuple(q.shape)}, k {tuple(k.shape)}: they differ in "
+                             "more than the head count")
+        if H % H_kv != 0:
+            raise ValueError(f"k's head count {H_kv} must divide q's {H}")
+    return B, H, H_kv, T, d
+
+
+def _rope_tables(cos: torch.Tensor, sin: torch.Tensor, T: int, d: int) -> None:
+    _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
+    _require(sin, "sin", cos.shape, torch.float32)
+    if cos.shape[0] < T:
+        raise ValueError("rope tables are shorter than the sequence")
+
+
+def _lse(lse: torch.Tensor | None, want: bool, B: int, H: int, T: int, device):
+    if lse is None and want:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=device)
+    if lse is not None:
+        _require(lse, "lse", (B, H, T), torch.float32)
+    return lse
+
+
 def sssl_windows(T: int, n_layer: int, pattern: str = "SSSL") -> list[int]:
     """Per-layer windows of a layer pattern (host-only C call)."""
     lib = _lib.load()
@@ -58,128 +97,114 @@ def rope_table(T: int, d: int, base: float = 10000.0, device=None) -> tuple[torc
 
 def qknorm_rope(q: torch.Tensor | None, k: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
                 eps: float = 1e-6, q_out: torch.Tensor | None = None,
-                k_out: torch.Tensor | None = None):
-    """QK-RMSNorm + RoPE of q, k [B, H, T, d]; outputs may be q, k themselves (in place).
+                k_out: torch.Tensor | None = None, layout: str = "bhtd"):
+    """QK-RMSNorm + RoPE of q [B, H, T, d] and k [B, H_kv, T, d] (or [B, T, H, d] and
+    [B, T, H_kv, d] with layout "bthd"); outputs may be q, k themselves (in place).
     With q None only k is processed (the returned q_out is None)."""
     lib = _lib.load()
     _require(k, "k")
-    if k.dim() != 4 or k.dtype not in _DTYPES:
-        raise ValueError("k must be [B, H, T, d] bf16 or fp32")
-    B, H, T, d = k.shape
+    if k.dtype not in _DTYPES:
+        raise ValueError("k must be bf16 or fp32")
     if q is not None:
-        _require(q, "q", k.shape, k.dtype)
-    _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
-    _require(sin, "sin", cos.shape, torch.float32)
-    if cos.shape[0] < T:
-        raise ValueError("rope tables are shorter than the sequence")
+        _require(q, "q", dtype=k.dtype)
+    B, H, H_kv, T, d = _geometry(q, k, layout)
+    _rope_tables(cos, sin, T, d)
     if q is not None:
         q_out = torch.empty_like(q) if q_out is None else q_out
-        _require(q_out, "q_out", k.shape, k.dtype)
+        _require(q_out, "q_out", q.shape, q.dtype)
     else:
         q_out = None
     k_out = torch.empty_like(k) if k_out is None else k_out
     _require(k_out, "k_out", k.shape, k.dtype)
-    rc = lib.attn_qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin),
-                              B, H, T, d, float(eps), _DTYPES[k.dtype], _stream_handle())
-    _lib.check("attn_qknorm_rope", rc)
+    rc = lib.attn_qknorm_rope_ex(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin),
+                                 B, H, H_kv, T, d, _LAYOUTS[layout], float(eps), _DTYPES[k.dtype],
+                                 _stream_handle())
+    _lib.check("attn_qknorm_rope_ex", rc)
     return q_out, k_out
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int = -1,
              causal: bool = True, out: torch.Tensor | None = None,
-             lse: torch.Tensor | None = None, want_lse: bool = True):
-    """softmax(q k^T / sqrt(d) + mask) v and its logsumexp for [B, H, T, d] tensors.
+             lse: torch.Tensor | None = None, want_lse: bool = True, layout: str = "bhtd"):
+    """softmax(q k^T / sqrt(d) + mask) v and its logsumexp. q is [B, H, T, d], k and v
+    [B, H_kv, T, d] with H_kv dividing H (or [B, T, heads, d] with layout "bthd").
 
-    Returns (out, lse); lse is fp32 [B, H, T] (None when want_lse is False and none was given).
+    Returns (out, lse); out has q's shape, lse is fp32 [B, H, T] (None when want_lse is False
+    and none was given).
     """
     lib = _lib.load()
     _require(q, "q")
-    if q.dim() != 4 or q.dtype not in _DTYPES:
-        raise ValueError("q must be [B, H, T, d] bf16 or fp32")
-    B, H, T, d = q.shape
-    _require(k, "k", q.shape, q.dtype)
-    _require(v, "v", q.shape, q.dtype)
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bf16 or fp32")
+    _require(k, "k", dtype=q.dtype)
+    B, H, H_kv, T, d = _geometry(q, k, layout)
+    _require(v, "v", k.shape, q.dtype)
     out = torch.empty_like(q) if out is None else out
     _require(out, "out", q.shape, q.dtype)
-    if lse is None and want_lse:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", (B, H, T), torch.float32)
-    rc = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, T, d, int(window),
-                      int(bool(causal)), _DTYPES[q.dtype], _stream_handle())
-    _lib.check("attn_fwd", rc)
+    lse = _lse(lse, want_lse, B, H, T, q.device)
+    rc = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, T, d,
+                         _LAYOUTS[layout], int(window), int(bool(causal)), _DTYPES[q.dtype],
+                         _stream_handle())
+    _lib.check("attn_fwd_ex", rc)
     return out, lse
 
 
 def attn_fwd_qnorm(q: torch.Tensor, kn: torch.Tensor, v: torch.Tensor, cos: torch.Tensor,
                    sin: torch.Tensor, window: int = -1, causal: bool = True, eps: float = 1e-6,
                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                   want_lse: bool = True):
+                   want_lse: bool = True, layout: str = "bhtd"):
     """Attention of raw bf16 q (normalised and rotated inside the kernel) against already
-    normalised and rotated keys kn. Returns (out, lse)."""
+    normalised and rotated keys kn. Shapes as in attn_fwd. Returns (out, lse)."""
     lib = _lib.load()
     _require(q, "q", dtype=torch.bfloat16)
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, T, d]")
-    B, H, T, d = q.shape
-    _require(kn, "kn", q.shape, q.dtype)
-    _require(v, "v", q.shape, q.dtype)
-    _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
-    _require(sin, "sin", cos.shape, torch.float32)
-    if cos.shape[0] < T:
-        raise ValueError("rope tables are shorter than the sequence")
+    _require(kn, "kn", dtype=q.dtype)
+    B, H, H_kv, T, d = _geometry(q, kn, layout)
+    _require(v, "v", kn.shape, q.dtype)
+    _rope_tables(cos, sin, T, d)
     out = torch.empty_like(q) if out is None else out
     _require(out, "out", q.shape, q.dtype)
-    if lse is None and want_lse:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", (B, H, T), torch.float32)
-    rc = lib.attn_fwd_qnorm(_ptr(q), _ptr(kn), _ptr(v), _ptr(out), _ptr(lse), _ptr(cos),
-                            _ptr(sin), B, H, T, d, float(eps), int(window), int(bool(causal)),
-                            _lib.ATTN_BF16, _stream_handle())
-    _lib.check("attn_fwd_qnorm", rc)
+    lse = _lse(lse, want_lse, B, H, T, q.device)
+    rc = lib.attn_fwd_qnorm_ex(_ptr(q), _ptr(kn), _ptr(v), _ptr(out), _ptr(lse), _ptr(cos),
+                               _ptr(sin), B, H, H_kv, T, d, _LAYOUTS[layout], float(eps),
+                               int(window), int(bool(causal)), _lib.ATTN_BF16, _stream_handle())
+    _lib.check("attn_fwd_qnorm_ex", rc)
     return out, lse
 
 
 def attn_fwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torch.Tensor,
                     sin: torch.Tensor, window: int = -1, causal: bool = True, eps: float = 1e-6,
                     k_work: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                    lse: torch.Tensor | None = None, want_lse: bool = True):
-    """QK-norm + RoPE of raw bf16 q, k and attention in one library call.
+                    lse: torch.Tensor | None = None, want_lse: bool = True,
+                    layout: str = "bhtd"):
+    """QK-norm + RoPE of raw bf16 q, k and attention in one library call. Shapes as in attn_fwd.
 
     Returns (out, lse, k_work); k_work holds RoPE(RMSNorm(k)) (it may be ``k`` itself).
     """
     lib = _lib.load()
     _require(q, "q", dtype=torch.bfloat16)
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, T, d]")
-    B, H, T, d = q.shape
-    _require(k, "k", q.shape, q.dtype)
-    _require(v, "v", q.shape, q.dtype)
-    _require(cos, "cos", (cos.shape[0], d // 2), torch.float32)
-    _require(sin, "sin", cos.shape, torch.float32)
-    if cos.shape[0] < T:
-        raise ValueError("rope tables are shorter than the sequence")
+    _require(k, "k", dtype=q.dtype)
+    B, H, H_kv, T, d = _geometry(q, k, layout)
+    _require(v, "v", k.shape, q.dtype)
+    _rope_tables(cos, sin, T, d)
     k_work = torch.empty_like(k) if k_work is None else k_work
-    _require(k_work, "k_work", q.shape, q.dtype)
+    _require(k_work, "k_work", k.shape, q.dtype)
     out = torch.empty_like(q) if out is None else out
     _require(out, "out", q.shape, q.dtype)
-    if lse is None and want_lse:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", (B, H, T), torch.float32)
-    rc = lib.attn_fwd_qknorm(_ptr(q), _ptr(k), _ptr(v), _ptr(k_work), _ptr(out), _ptr(lse),
-                             _ptr(cos), _ptr(sin), B, H, T, d, float(eps), int(window),
-                             int(bool(causal)), _lib.ATTN_BF16, _stream_handle())
-    _lib.check("attn_fwd_qknorm", rc)
+    lse = _lse(lse, want_lse, B, H, T, q.device)
+    rc = lib.attn_fwd_qknorm_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(k_work), _ptr(out), _ptr(lse),
+                                _ptr(cos), _ptr(sin), B, H, H_kv, T, d, _LAYOUTS[layout],
+                                float(eps), int(window), int(bool(causal)), _lib.ATTN_BF16,
+                                _stream_handle())
+    _lib.check("attn_fwd_qknorm_ex", rc)
     return out, lse, k_work
 
 
 def attention_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torch.Tensor,
                     sin: torch.Tensor, window: int = -1, eps: float = 1e-6,
                     qn: torch.Tensor | None = None, kn: torch.Tensor | None = None,
-                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                    layout: str = "bhtd"):
     """One attention layer: QK-norm + RoPE of raw q, k, then causal attention with ``window``
-    (two calls: attn_qknorm_rope writes the normalised q and k, attn_fwd reads them)."""
-    qn, kn = qknorm_rope(q, k, cos, sin, eps, qn, kn)
-    return attn_fwd(qn, kn, v, window=window, causal=True, out=out, lse=lse)
+    (two calls: attn_qknorm_rope_ex writes the normalised q and k, attn_fwd_ex reads them)."""
+    qn, kn = qknorm_rope(q, k, cos, sin, eps, qn, kn, layout=layout)
+    return attn_fwd(qn, kn, v, window=window, causal=True, out=out, lse=lse, layout=layout)
