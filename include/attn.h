@@ -199,7 +199,7 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, v
  * The bf16 attention kernels address one head's rows through 32-bit byte offsets: for
  * ATTN_BF16, (T + 128) * (largest row stride in bytes) must be below 2^31, else ATTN_ERR_SHAPE
  * (row stride: d * 2 for ATTN_LAYOUT_BHTD, H * d * 2 for q and H_kv * d * 2 for k, v in
- * ATTN_LAYOUT_BTHD).
+ * ATTN_LAYOUT_BTHD). Every entry point also needs H * d < 2^24, else ATTN_ERR_SHAPE.
  */
 int attn_qknorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
                         const float* cos_tab, const float* sin_tab, int B, int H, int H_kv, int T,

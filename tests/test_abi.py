@@ -387,3 +387,13 @@ def test_binding_geometry():
         _geometry(q, k, "tbhd")
     with pytest.raises(ValueError):
         _geometry(q, k, "bthd")  # read as [B, T, H, d], the shapes disagree
+
+
+@no_gpu
+def test_row_width_limit(lib):
+    # H * d must stay below 2^24 elements (the prologue's per-block row offsets are 32-bit)
+    a = qkn_args(H=1 << 18, H_kv=1 << 18, T=1, d=64, **{n: (i + 1) << 40 for i, n in enumerate(
+        ("q", "k", "qo", "ko", "cos", "sin"))}, eps=-1.0)
+    assert _qkn_ex(lib, a) == _lib.ATTN_ERR_SHAPE
+    a["H"] = a["H_kv"] = (1 << 18) - 1  # just below: reaches the eps rule
+    assert _qkn_ex(lib, a) == _lib.ATTN_ERR_ARG

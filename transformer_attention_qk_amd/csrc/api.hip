@@ -30,8 +30,9 @@ int check_dims(int B, int H, int H_kv, int T, int d, int layout, attn::Dims* dm,
   if (bh > 0x7fffffff) return ATTN_ERR_SHAPE;
   const int64_t rows = bh * T;
   if (rows > kMaxElems / 256) return ATTN_ERR_SHAPE;
-  // A row stride of the [B][T][H][d] order (H * d elements) must fit an int.
-  if ((int64_t)H * d > 0x3fffffff) return ATTN_ERR_SHAPE;
+  // Row strides of the [B][T][H][d] order (H * d elements) stay below 2^24, so that the offsets
+  // of a block of up to 128 rows fit an int.
+  if ((int64_t)H * d >= (int64_t(1) << 24)) return ATTN_ERR_SHAPE;
   *n_q = rows * d;
   *n_kv = (int64_t)B * H_kv * T * d;
   *dm = attn::Dims{B, H, H_kv, T, d, layout};

@@ -597,9 +597,10 @@ template <int D, int MODE, bool QKN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
-    const float* __restrict__ sin_tab, float eps, Geometry geo, int BH, int T, int window_arg,
-    float scale_log2, int nqt) {
+    const float* __restrict__ sin_tab, float eps, Geometry geo, FastDiv fd_bh, int T,
+    int window_arg, float scale_log2, int nqt) {
   using C = FwdCfg<D>;
+  const int BH = (int)fd_bh.d;  // heads B * H; items are (head, query block) pairs
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::STREAM_LDS];
   const int tid = threadIdx.x;
@@ -617,8 +618,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   // Items of this workgroup: heaviest-first ranks dealt out in snake order.
   auto rank_of = [&](int k) { return k * P + ((k & 1) ? (P - 1 - g) : g); };
   auto decode = [&](int rank, int& bh, int& q0, int& tb, int& te) {
-    bh = rank % BH;
-    q0 = (nqt - 1 - rank / BH) * C::BM;
+    const int qb = (int)fd_bh.div((uint32_t)rank);
+    bh = rank - qb * BH;
+    q0 = (nqt - 1 - qb) * C::BM;
     item_tiles<D, MODE>(q0, T, window, tb, te);
   };
 
@@ -955,7 +957,8 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
     const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
     hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN>), dim3(grid), dim3(256), 0, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse,
-                       a.cos_tab, a.sin_tab, a.eps, a.geo, BH, a.T, a.window, scale_log2, nqt);
+                       a.cos_tab, a.sin_tab, a.eps, a.geo, make_fastdiv((uint32_t)BH), a.T,
+                       a.window, scale_log2, nqt);
   } else {
     hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE, QKN>), dim3((unsigned)n_items), dim3(256), 0,
                        stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out,

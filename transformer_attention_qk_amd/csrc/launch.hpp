@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace attn {
 
 // Shape of one call: q and out are [B, H, T, d], k and v [B, H_kv, T, d] (H_kv divides H), all
@@ -21,12 +23,14 @@ struct Strides {
 };
 struct Geometry {
   Strides q, kv;
-  int H, group;
+  FastDiv H, group;  // query heads, and query heads per kv head
   __host__ __device__ __forceinline__ int64_t q_head(int bh) const {
-    return (int64_t)(bh / H) * q.b + (int64_t)(bh % H) * q.h;
+    const uint32_t b = H.div((uint32_t)bh), h = (uint32_t)bh - b * H.d;
+    return (int64_t)b * q.b + (int64_t)h * q.h;
   }
   __host__ __device__ __forceinline__ int64_t kv_head(int bh) const {
-    return (int64_t)(bh / H) * kv.b + (int64_t)((bh % H) / group) * kv.h;
+    const uint32_t b = H.div((uint32_t)bh), h = (uint32_t)bh - b * H.d;
+    return (int64_t)b * kv.b + (int64_t)group.div(h) * kv.h;
   }
 };
 
@@ -40,8 +44,8 @@ inline Geometry make_geometry(const Dims& dm) {
     g.q = Strides{(int64_t)dm.T * dm.H * d, d, (int)(dm.H * d)};
     g.kv = Strides{(int64_t)dm.T * dm.H_kv * d, d, (int)(dm.H_kv * d)};
   }
-  g.H = dm.H;
-  g.group = dm.H / dm.H_kv;
+  g.H = make_fastdiv((uint32_t)dm.H);
+  g.group = make_fastdiv((uint32_t)(dm.H / dm.H_kv));
   return g;
 }
 

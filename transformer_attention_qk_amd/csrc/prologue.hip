@@ -88,22 +88,49 @@ template <typename Elem, int D, int R>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const Elem* __restrict__ q, const Elem* __restrict__ k, Elem* q_out, Elem* k_out,
     const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, Strides sq, Strides sk,
-    int H, int H_kv, int heads_q, int heads, int T, int t_blocks, float eps) {
+    FastDiv H, FastDiv H_kv, int heads_q, int heads, int T, FastDiv t_blocks, float eps) {
   constexpr int E = kE<Elem>;
   constexpr int HALF = D / 2;
   constexpr int L = D / E;      // lanes per row (2 .. 32)
   constexpr int TPB = 256 / L;  // positions per block
-  const int tb = (int)(blockIdx.x % (unsigned)t_blocks);
-  const int h0 = (int)(blockIdx.x / (unsigned)t_blocks) * R;
-  const int t = tb * TPB + (int)threadIdx.x / L;
+  const int hb = (int)t_blocks.div(blockIdx.x);
+  const int tb = (int)blockIdx.x - hb * (int)t_blocks.d;
+  const int h0 = hb * R;
+  const int t_loc = (int)threadIdx.x / L;
+  const int t0 = tb * TPB;
+  // Positions past T (in the last block of positions) redo row T - 1 and store nothing. All L
+  // lanes of a row group share t, so the xor shuffles below never mix rows.
+  const bool valid = t0 + t_loc < T;
+  const int t = valid ? t0 + t_loc : T - 1;
+  const int r_loc = t - t0;  // row of t within the block
   const int sub = (int)threadIdx.x % L;
-  // All L lanes of a row group share t, so a group is either fully active or fully inactive and
-  // the xor shuffles below never read a lane of another row.
-  if (t >= T) return;
   const bool first = sub < L / 2;
   const int j0 = (sub % (L / 2)) * E;  // frequency of the chunk's first element
   const int total = heads_q + heads;
 
+  // A row's element offset splits into a block-uniform part (head h at position t0) and this
+  // lane's part, which stays below 2^31 (TPB row strides; the host bounds H * d).
+  auto head_base = [&](int h) -> int64_t {
+    if (h < heads_q) {
+      const uint32_t b = H.div((uint32_t)h);
+      return (int64_t)b * sq.b + (int64_t)(h - b * H.d) * sq.h + (int64_t)t0 * sq.t;
+    }
+    const uint32_t hk = (uint32_t)(h - heads_q), b = H_kv.div(hk);
+    return (int64_t)b * sk.b + (int64_t)(hk - b * H_kv.d) * sk.h + (int64_t)t0 * sk.t;
+  };
+  const int lane_q = r_loc * sq.t + sub * E, lane_k = r_loc * sk.t + sub * E;
+  u32x4 raw[R];
+  int64_t base[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int h = h0 + r;  // block-uniform
+    if (h < total) {
+      base[r] = head_base(h);
+      const Elem* src = (h < heads_q) ? q + base[r] + lane_q : k + base[r] + lane_k;
+      raw[r] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+  // The rotation factors of position t, loaded after the rows so those go out first.
   float c[E], s[E];
   const float* ct = cos_tab + (int64_t)t * HALF + j0;
   const float* st = sin_tab + (int64_t)t * HALF + j0;
@@ -111,22 +138,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   for (int i = 0; i < E; i += 4) {
     Vec<float, 4>::load(ct + i, c + i);
     Vec<float, 4>::load(st + i, s + i);
-  }
-  // Element offset of row t of head h (block-uniform apart from t).
-  auto row = [&](int h) -> int64_t {
-    if (h < heads_q) return (int64_t)(h / H) * sq.b + (int64_t)(h % H) * sq.h + (int64_t)t * sq.t;
-    const int hk = h - heads_q;
-    return (int64_t)(hk / H_kv) * sk.b + (int64_t)(hk % H_kv) * sk.h + (int64_t)t * sk.t;
-  };
-  u32x4 raw[R];
-  int64_t off[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int h = h0 + r;  // block-uniform
-    if (h < total) {
-      off[r] = row(h) + sub * E;
-      raw[r] = *reinterpret_cast<const u32x4*>((h < heads_q ? q : k) + off[r]);
-    }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -151,7 +162,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
       // first half: x_j cos + x_{j+h} sin; second half: -x_j sin + x_{j+h} cos
       y[i] = first ? fmaf(a, c[i], b * s[i]) : fmaf(a, c[i], -(b * s[i]));
     }
-    Vec<Elem, E>::store((h < heads_q ? q_out : k_out) + off[r], y);
+    if (valid)
+      Vec<Elem, E>::store((h < heads_q) ? q_out + base[r] + lane_q : k_out + base[r] + lane_k, y);
   }
 }
 
@@ -170,7 +182,8 @@ static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out
   const int64_t grid = (int64_t)t_blocks * ((heads_q + heads + R - 1) / R);
   hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
                      (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, cos_tab, sin_tab,
-                     geo.q, geo.kv, dm.H, dm.H_kv, heads_q, heads, T, t_blocks, eps);
+                     geo.q, geo.kv, make_fastdiv((uint32_t)dm.H), make_fastdiv((uint32_t)dm.H_kv),
+                     heads_q, heads, T, make_fastdiv((uint32_t)t_blocks), eps);
   return hipGetLastError();
 }
 
