@@ -14,6 +14,10 @@ The value is counted the way the metric names it: TFLOP/s of unmasked attention 
 (4 d FLOPs per visible (query, key) pair) over the whole step's time, prologue included.
 It prints ONE JSON line on stdout.
 
+--workload autoresearch_default times the train.py listing's default model instead (B=128, H=4,
+T=2048, d=128, eight layers "SSSL" with windows 1024 / 2048) on q, k, v in the projections'
+[B][T][H][d] order, and prints its own JSON line (metric named after that shape).
+
 Extra modes (used to collect rocprofv3 counters; they print no JSON):
   --only attn|kprologue|attn_unfused|prologue   run only that kernel, --steps times per layer
   --copy-calibration     run a plain 256 MiB device copy (known bytes) for counter scaling
@@ -84,19 +88,16 @@ def measured_traffic() -> float | None:
     return float(val.group(1))
 
 
-def cpu_baseline(index: int, windows: list[int], budget_s: float) -> dict:
+def cpu_baseline(w, layer_inputs, windows: list[int], budget_s: float) -> dict:
     """The fp64 oracle on a bounded sample of the same workload: whole heads, all layers, in
     (b, h) order, until the time budget is spent. Returns TFLOP/s on the same unmasked-FLOP
-    numerator as the GPU."""
+    numerator as the GPU. layer_inputs: each layer's CPU q, k, v in [B, H, T, d] order."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
 
     import oracle
-    from transformer_attention_qk_amd import inputs
 
-    w = inputs.WORKLOADS[index]
-    layer_inputs = [inputs.make_qkv(index, l) for l in range(len(windows))]
     flops = 0
     heads = 0
     elapsed = 0.0
@@ -131,8 +132,9 @@ def cpu_baseline(index: int, windows: list[int], budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; 20 for autoresearch_default)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3)")
     ap.add_argument("--workload", default="andrea120m_sssl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -162,28 +164,43 @@ def main() -> int:
         n = 256 << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(max(1, args.steps)):
+        for _ in range(max(1, args.steps or 1)):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"copy calibration: {max(1, args.steps)} copies of {n} bytes read + {n} bytes written",
+        print(f"copy calibration: {max(1, args.steps or 1)} copies of {n} bytes read + {n} bytes written",
               file=sys.stderr)
         return 0
 
-    index = [w.name for w in inputs.WORKLOADS].index(args.workload)
-    w = inputs.WORKLOADS[index]
+    names = [w.name for w in inputs.WORKLOADS] + [inputs.MODEL_DEFAULT.name]
+    if args.workload not in names:
+        print(f"unknown workload {args.workload!r}; one of {names}", file=sys.stderr)
+        return 2
+    index = names.index(args.workload)
+    w = inputs.workload(index)
     if w.dtype != "bf16":
         print("the bench times bf16 workloads", file=sys.stderr)
         return 2
+    model_default = index == inputs.MODEL_DEFAULT_INDEX
+    if args.steps is None:
+        args.steps = 20 if model_default else 200
+    if args.warmup is None:
+        args.warmup = 3 if model_default else 20
+    layout = "bthd" if model_default else "bhtd"  # the listing's projections give [B][T][H][d]
     windows = ops.sssl_windows(w.T, w.n_layer, w.pattern)
     L = len(windows)
 
-    # Inputs resident in HBM, one set of buffers per layer.
-    q, k, v, qn, kn, out, lse = ([] for _ in range(7))
+    # Inputs resident in HBM, one set of buffers per layer (drawn in [B, H, T, d] order, stored
+    # in the layout the workload runs in).
+    q, k, v, qn, kn, out, lse, cpu_inputs = ([] for _ in range(8))
     for l in range(L):
         ql, kl, vl = inputs.make_qkv(index, l)
-        q.append(ql.cuda())
-        k.append(kl.cuda())
-        v.append(vl.cuda())
+        if not args.no_cpu_baseline:
+            cpu_inputs.append((ql, kl, vl))
+        for dst, x in ((q, ql), (k, kl), (v, vl)):
+            x = x.cuda()
+            dst.append((x.transpose(1, 2) if layout == "bthd" else x).contiguous())
+            del x
+        del ql, kl, vl
         qn.append(torch.empty_like(q[-1]))
         kn.append(torch.empty_like(k[-1]))
         out.append(torch.empty_like(q[-1]))
@@ -203,30 +220,34 @@ def main() -> int:
     pcos, psin = cos.data_ptr(), sin.data_ptr()
     B, H, T, d = w.B, w.H, w.T, w.d
     bf16 = _lib.ATTN_BF16
+    lay = _lib.ATTN_LAYOUT_BTHD if layout == "bthd" else _lib.ATTN_LAYOUT_BHTD
 
     # The layer as one call, and its two kernels as separate calls (the same launches).
     def layer(l):
         pq, pk, pv, _, pkn, po, pl = P[l]
-        return lib.attn_fwd_qknorm(pq, pk, pv, pkn, po, pl, pcos, psin, B, H, T, d, eps,
-                                   windows[l], 1, bf16, stream)
+        return lib.attn_fwd_qknorm_ex(pq, pk, pv, pkn, po, pl, pcos, psin, B, H, H, T, d, lay,
+                                      eps, windows[l], 1, bf16, stream)
 
     def kprologue(l):
         _, pk, _, _, pkn, _, _ = P[l]
-        return lib.attn_qknorm_rope(None, pk, None, pkn, pcos, psin, B, H, T, d, eps, bf16, stream)
+        return lib.attn_qknorm_rope_ex(None, pk, None, pkn, pcos, psin, B, H, H, T, d, lay, eps,
+                                       bf16, stream)
 
     def attention(l):
         pq, _, pv, _, pkn, po, pl = P[l]
-        return lib.attn_fwd_qnorm(pq, pkn, pv, po, pl, pcos, psin, B, H, T, d, eps, windows[l], 1,
-                                  bf16, stream)
+        return lib.attn_fwd_qnorm_ex(pq, pkn, pv, po, pl, pcos, psin, B, H, H, T, d, lay, eps,
+                                     windows[l], 1, bf16, stream)
 
     # The two-call path.
     def prologue(l):
         pq, pk, _, pqn, pkn, _, _ = P[l]
-        return lib.attn_qknorm_rope(pq, pk, pqn, pkn, pcos, psin, B, H, T, d, eps, bf16, stream)
+        return lib.attn_qknorm_rope_ex(pq, pk, pqn, pkn, pcos, psin, B, H, H, T, d, lay, eps,
+                                       bf16, stream)
 
     def attention_unfused(l):
         _, _, pv, pqn, pkn, po, pl = P[l]
-        return lib.attn_fwd(pqn, pkn, pv, po, pl, B, H, T, d, windows[l], 1, bf16, stream)
+        return lib.attn_fwd_ex(pqn, pkn, pv, po, pl, B, H, H, T, d, lay, windows[l], 1, bf16,
+                               stream)
 
     if args.only:
         # inputs of the chosen kernel only, so a counter run sees no other kernel of its kind
@@ -251,7 +272,7 @@ def main() -> int:
     layer(0)
     ref_out = out[0].clone()
     ops.attn_fwd_qknorm(q[0], k[0], v[0], cos, sin, window=windows[0], eps=eps, k_work=kn[0],
-                        out=out[0], lse=lse[0])
+                        out=out[0], lse=lse[0], layout=layout)
     torch.cuda.synchronize()
     if not torch.equal(ref_out, out[0]):
         print("bench: binding and direct call disagree", file=sys.stderr)
@@ -318,10 +339,14 @@ def main() -> int:
     attn_bytes = attn_compulsory_bytes(w.B, w.H, w.T, w.d)
     kpro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=1)
     pro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=2)
-    traffic = measured_traffic()
+    traffic = measured_traffic() if not model_default else None
+    kernel = (f"attn_fwd_bf16_stream<{w.d}, mode, qkn=true>" if w.d <= 64
+              else f"attn_fwd_bf16_tile<{w.d}, mode, qkn=true>")
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not model_default else (
+            "bf16 causal/SWA attention fwd TFLOP/s + % MFMA peak, train.py default model "
+            "B=128 H=4 T=2048 d=128 [B,T,H,D]"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -335,7 +360,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "layers": L,
-            "windows": windows,
+            "windows": windows, "layout": layout,
             "step": "per layer: attn_fwd_qknorm (k-only qknorm_rope kernel + attention kernel "
                     "with in-kernel q norm and rotation)",
             "flops_per_step": step_flops,
@@ -343,7 +368,7 @@ def main() -> int:
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_stream<64, mode, qkn=true>",
+            "kernel": kernel,
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -372,7 +397,7 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(index, windows, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, cpu_inputs, windows, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
 
