@@ -17,3 +17,10 @@ from .attention import (  # noqa: F401
     sssl_windows,
     visible,
 )
+from .backward import (  # noqa: F401
+    attention_backward,
+    attention_layer_backward,
+    qknorm_rope_backward,
+    rms_norm_backward,
+    rope_apply_backward,
+)

@@ -353,6 +353,145 @@ def check_gqa_head_mapping(o, seed=10):
         assert np.array_equal(out[:, h:h + 1], o1) and np.array_equal(lse[:, h:h + 1], l1)
 
 
+# ---------------------------------------------------------------------------------------------
+# Backward pass (R14): the gradients are pinned to the forward oracle through finite
+# differences, to autograd of torch's own attention and norm routines, and to invariants.
+# ---------------------------------------------------------------------------------------------
+
+def _fd_grad(f, x, h=1e-6):
+    """Central differences of the scalar f at x (fp64), one element at a time."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + h
+        fp = f()
+        x[i] = old - h
+        fm = f()
+        x[i] = old
+        g[i] = (fp - fm) / (2 * h)
+    return g
+
+
+def check_backward_finite_differences(o, seed=11):
+    """attention_backward against central differences of attention's loss sum(dout * O), for
+    multi-head and grouped heads, windows and the non-causal mask."""
+    rng = _rng(seed)
+    for (B, H, H_kv, T, d, window, causal) in [(1, 2, 2, 5, 4, -1, True), (1, 2, 1, 6, 4, 2, True),
+                                               (2, 4, 2, 4, 2, 0, True), (1, 1, 1, 4, 3, -1, False)]:
+        q = rng.standard_normal((B, H, T, d))
+        k = rng.standard_normal((B, H_kv, T, d))
+        v = rng.standard_normal((B, H_kv, T, d))
+        do = rng.standard_normal((B, H, T, d))
+        loss = lambda: float(np.sum(o.attention(q, k, v, window=window, causal=causal)[0] * do))
+        dq, dk, dv = o.attention_backward(q, k, v, do, window=window, causal=causal)
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            assert np.allclose(g, _fd_grad(loss, x), rtol=0, atol=2e-8), (B, H, H_kv, T, window)
+
+
+def check_layer_backward_finite_differences(o, seed=12):
+    """attention_layer_backward (prologue included) against central differences of
+    attention_layer's loss, on raw rows of several scales."""
+    rng = _rng(seed)
+    for (H, H_kv, T, d, window, scale) in [(2, 2, 5, 4, -1, 1.0), (2, 1, 6, 4, 2, 3.0),
+                                           (1, 1, 3, 8, -1, 0.1)]:
+        q = scale * rng.standard_normal((1, H, T, d))
+        k = scale * rng.standard_normal((1, H_kv, T, d))
+        v = rng.standard_normal((1, H_kv, T, d))
+        do = rng.standard_normal((1, H, T, d))
+        loss = lambda: float(np.sum(o.attention_layer(q, k, v, window=window)[0] * do))
+        dq, dk, dv = o.attention_layer_backward(q, k, v, do, window=window)
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            assert np.allclose(g, _fd_grad(loss, x), rtol=0, atol=2e-7 / scale), (H, H_kv, T)
+
+
+def check_backward_torch_autograd(o, seed=13):
+    """Library special case: torch's scaled_dot_product_attention with an explicit boolean mask
+    and torch's rms_norm, differentiated by autograd in float64 on the CPU; the rotation is
+    applied as multiplication of the pairs (x_j + i x_{j+d/2}) by exp(-i theta)."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(seed)
+    B, H, H_kv, T, d = 2, 4, 2, 37, 8
+    for window, causal in ((-1, True), (5, True), (-1, False)):
+        arrs = [rng.standard_normal(s) for s in ((B, H, T, d), (B, H_kv, T, d), (B, H_kv, T, d),
+                                                (B, H, T, d))]
+        q, k, v, do = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in arrs)
+        i = torch.arange(T)[:, None]
+        j = torch.arange(T)[None, :]
+        mask = torch.ones(T, T, dtype=torch.bool)
+        if causal:
+            mask = j <= i
+            if window >= 0:
+                mask = mask & (i - j <= window)
+        g = H // H_kv
+        theta = torch.outer(torch.arange(T, dtype=torch.float64),
+                            10000.0 ** (-torch.arange(0, d, 2, dtype=torch.float64) / d))
+
+        def rot(x):
+            z = torch.complex(x[..., : d // 2], x[..., d // 2:]) * torch.polar(
+                torch.ones_like(theta), -theta)
+            return torch.cat([z.real, z.imag], dim=-1)
+
+        for layer in (False, True):
+            qq, kk = (rot(F.rms_norm(q, (d,), eps=1e-6)), rot(F.rms_norm(k, (d,), eps=1e-6))) \
+                if layer else (q, k)
+            out = F.scaled_dot_product_attention(qq, kk.repeat_interleave(g, dim=1),
+                                                 v.repeat_interleave(g, dim=1), attn_mask=mask)
+            gq, gk, gv = torch.autograd.grad((out * do.detach()).sum(), (q, k, v))
+            args = [a.detach().numpy() for a in (q, k, v, do)]
+            fn = o.attention_layer_backward if layer else o.attention_backward
+            dq, dk, dv = fn(*args, window=window, causal=causal)
+            for mine, ref in ((dq, gq), (dk, gk), (dv, gv)):
+                assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-11), (window, causal, layer)
+
+
+def check_backward_invariants(o, seed=14):
+    """Exact properties of the gradients: every row of dS sums to zero, so the keys' gradients
+    of a head sum to zero; with window 0 each query sees only its own key, so dq = dk = 0 and
+    dv = dout; the norm's gradient is orthogonal to the row when eps = 0 (the norm is then scale
+    invariant); the rotation's backward keeps each pair's length."""
+    rng = _rng(seed)
+    B, H, H_kv, T, d = 2, 4, 2, 19, 8
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, H_kv, T, d))
+    v = rng.standard_normal((B, H_kv, T, d))
+    do = rng.standard_normal((B, H, T, d))
+    for window in (-1, 4):
+        dq, dk, dv = o.attention_backward(q, k, v, do, window=window)
+        assert np.allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12)
+    k2 = rng.standard_normal((B, H, T, d))
+    v2 = rng.standard_normal((B, H, T, d))
+    dq, dk, dv = o.attention_backward(q, k2, v2, do, window=0)
+    assert np.allclose(dq, 0.0, atol=1e-14) and np.allclose(dk, 0.0, atol=1e-14)
+    assert np.allclose(dv, do, rtol=0, atol=1e-14)
+    x = 3.0 * rng.standard_normal((5, 16))
+    g = rng.standard_normal((5, 16))
+    dx = o.rms_norm_backward(x, g, eps=0.0)
+    assert np.allclose(np.sum(dx * x, axis=-1), 0.0, atol=1e-12)
+    # a gradient along the output row itself maps to zero (eps = 0): d|xh|^2 is 0
+    xh = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+    assert np.allclose(o.rms_norm_backward(x, xh, eps=0.0), 0.0, atol=1e-12)
+    cos, sin = o.rope_cos_sin(7, 16)
+    gy = rng.standard_normal((7, 16))
+    gx = o.rope_apply_backward(gy, cos, sin)
+    n_in = gy[:, :8] ** 2 + gy[:, 8:] ** 2
+    n_out = gx[:, :8] ** 2 + gx[:, 8:] ** 2
+    assert np.allclose(n_in, n_out, rtol=1e-13, atol=0)
+    # and it undoes the forward rotation
+    assert np.allclose(o.rope_apply_backward(o.rope_apply(gy, cos, sin), cos, sin), gy, atol=1e-13)
+
+
+BACKWARD_CHECKS = [
+    check_backward_finite_differences,
+    check_layer_backward_finite_differences,
+    check_backward_torch_autograd,
+    check_backward_invariants,
+]
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_worked_example_qknorm,
@@ -369,4 +508,4 @@ ALL_CHECKS = [
     check_norm_rope_commute,
     check_sssl_windows,
     check_gqa_head_mapping,
-]
+] + BACKWARD_CHECKS

@@ -127,3 +127,95 @@ def _gqa_interleaved(q, k, v, window=-1, causal=True, rows=None, block=256):
 
 def test_gqa_mapping_mutation_is_caught():
     assert _fails(_mutant(attention=_gqa_interleaved), [pins.check_gqa_head_mapping])
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward pass: planted mistakes in copies of the gradient formulas.
+# ---------------------------------------------------------------------------------------------
+
+def _backward_with(keep_delta=True, p_factor=True, dk_scale=None, dq_scale=None, dv_transposed=False):
+    def bwd(q, k, v, do, window=-1, causal=True, block=256):
+        q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+        B, H, T, d = q.shape
+        H_kv = k.shape[1]
+        c = 1 / math.sqrt(d)
+        i = np.arange(T)[:, None]
+        j = np.arange(T)[None, :]
+        vis = oracle.visible(i, j, window, causal)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // H_kv)
+                s = np.where(vis, c * q[b, h] @ k[b, g].T, -np.inf)
+                p = np.exp(s - s.max(1, keepdims=True))
+                p /= p.sum(1, keepdims=True)
+                dp = do[b, h] @ v[b, g].T
+                D = (p * dp).sum(1, keepdims=True) if keep_delta else 0.0
+                ds = (p if p_factor else 1.0) * (dp - D) * vis
+                dv[b, g] += (p @ do[b, h]) if dv_transposed else (p.T @ do[b, h])
+                dq[b, h] += (dq_scale(d) if dq_scale else c) * ds @ k[b, g]
+                dk[b, g] += (dk_scale(d) if dk_scale else c) * ds.T @ q[b, h]
+        return dq, dk, dv
+    return bwd
+
+
+def _layer_bwd_with(att_bwd, pro_bwd=None):
+    def layer(q, k, v, do, window=-1, causal=True, eps=1e-6, base=10000.0):
+        qn, kn = oracle.qknorm_rope(q, k, eps, base)
+        dqn, dkn, dv = att_bwd(qn, kn, v, do, window, causal)
+        pb = pro_bwd or oracle.qknorm_rope_backward
+        return pb(q, dqn, eps, base), pb(k, dkn, eps, base), dv
+    return layer
+
+
+BWD_CHECKS = [pins.check_backward_finite_differences, pins.check_layer_backward_finite_differences,
+              pins.check_backward_torch_autograd, pins.check_backward_invariants]
+
+
+def test_unmutated_backward_copy_passes():
+    bwd = _backward_with()
+    o = _mutant(attention_backward=bwd, attention_layer_backward=_layer_bwd_with(bwd),
+                rms_norm_backward=oracle.rms_norm_backward,
+                rope_apply_backward=oracle.rope_apply_backward)
+    assert not _fails(o, BWD_CHECKS)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("no D subtracted", dict(keep_delta=False)),
+    ("dS without the P factor", dict(p_factor=False)),
+    ("dK without the 1/sqrt(d) scale", dict(dk_scale=lambda d: 1.0)),
+    ("dQ scaled by 1/d", dict(dq_scale=lambda d: 1.0 / d)),
+    ("dV from P instead of P^T", dict(dv_transposed=True)),
+])
+def test_backward_mutations_are_caught(name, kw):
+    bwd = _backward_with(**kw)
+    o = _mutant(attention_backward=bwd, attention_layer_backward=_layer_bwd_with(bwd),
+                rms_norm_backward=oracle.rms_norm_backward,
+                rope_apply_backward=oracle.rope_apply_backward)
+    assert _fails(o, BWD_CHECKS), name
+
+
+def _pro_bwd_rotation_sign(x, dy, eps=1e-6, base=10000.0):
+    """Prologue backward that rotates dy forward instead of back."""
+    T, d = np.asarray(x).shape[-2:]
+    cos, sin = oracle.rope_cos_sin(T, d, base)
+    return oracle.rms_norm_backward(x, oracle.rope_apply(dy, cos, sin), eps)
+
+
+def _pro_bwd_no_projection(x, dy, eps=1e-6, base=10000.0):
+    """Prologue backward that drops the norm's projection term (treats r as a constant)."""
+    x = np.asarray(x, np.float64)
+    T, d = x.shape[-2:]
+    cos, sin = oracle.rope_cos_sin(T, d, base)
+    r = 1 / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps)
+    return r * oracle.rope_apply_backward(dy, cos, sin)
+
+
+@pytest.mark.parametrize("name,fn", [("rotation forward in backward", _pro_bwd_rotation_sign),
+                                     ("norm backward without projection", _pro_bwd_no_projection)])
+def test_prologue_backward_mutations_are_caught(name, fn):
+    o = _mutant(attention_backward=oracle.attention_backward,
+                attention_layer_backward=_layer_bwd_with(oracle.attention_backward, fn),
+                rms_norm_backward=oracle.rms_norm_backward,
+                rope_apply_backward=oracle.rope_apply_backward)
+    assert _fails(o, BWD_CHECKS), name
