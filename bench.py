@@ -14,6 +14,9 @@ The value is counted the way the metric names it: TFLOP/s of unmasked attention 
 (4 d FLOPs per visible (query, key) pair) over the whole step's time, prologue included.
 It prints ONE JSON line on stdout.
 
+The JSON line also carries "backward": the same layers' gradients (attn_bwd_ex on the normalised
+q, k, then attn_qknorm_rope_bwd_ex), timed with events around each launch; context only.
+
 --workload autoresearch_default times the train.py listing's default model instead (B=128, H=4,
 T=2048, d=128, eight layers "SSSL" with windows 1024 / 2048) on q, k, v in the projections'
 [B][T][H][d] order, and prints its own JSON line (metric named after that shape).
@@ -137,6 +140,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3)")
     ap.add_argument("--workload", default="andrea120m_sssl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue"],
                     default=None)
@@ -331,6 +335,42 @@ def main() -> int:
     ms_per_step_unfused = time_steps(step_unfused)
     pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
 
+    # The backward pass (context, not the value): per layer, the gradient of sum(dout * out)
+    # through attn_bwd_ex on the normalised q, k the two-call path wrote (kernels: delta, dK/dV,
+    # dQ), then the prologue's backward attn_qknorm_rope_bwd_ex in place.
+    bwd_ms = None
+    if not args.no_backward:
+        dout, dq, dk, dv, delta = ([] for _ in range(5))
+        for l in range(L):
+            dout.append(inputs.make_random(tuple(q[l].shape), torch.bfloat16, 900 + l).cuda())
+            dq.append(torch.empty_like(q[l]))
+            dk.append(torch.empty_like(k[l]))
+            dv.append(torch.empty_like(v[l]))
+            delta.append(torch.empty_like(lse[l]))
+        for l in range(L):
+            _lib.check("prologue", prologue(l))
+            _lib.check("attn_unfused", attention_unfused(l))
+        torch.cuda.synchronize()
+        PB = [tuple(t.data_ptr() for t in (dout[l], dq[l], dk[l], dv[l], delta[l]))
+              for l in range(L)]
+
+        def attention_bwd(l):
+            _, _, pv, pqn, pkn, po, pl = P[l]
+            pdo, pdq, pdk, pdv, pdl = PB[l]
+            return lib.attn_bwd_ex(pqn, pkn, pv, po, pdo, pl, pdl, pdq, pdk, pdv, B, H, H, T, d,
+                                   lay, windows[l], 1, bf16, stream)
+
+        def prologue_bwd(l):
+            pq, pk, _, _, _, _, _ = P[l]
+            _, pdq, pdk, _, _ = PB[l]
+            return lib.attn_qknorm_rope_bwd_ex(pq, pk, pdq, pdk, pdq, pdk, pcos, psin, B, H, H, T,
+                                               d, lay, eps, bf16, stream)
+
+        for l in range(L):
+            _lib.check("attn_bwd", attention_bwd(l))
+            _lib.check("prologue_bwd", prologue_bwd(l))
+        bwd_ms, pro_bwd_ms = time_launches(attention_bwd, prologue_bwd)
+
     flops_layer = [attn_flops(w.B, w.H, w.T, w.d, W) for W in windows]
     step_flops = sum(flops_layer)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
@@ -396,6 +436,16 @@ def main() -> int:
             "prologue_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
         },
     }
+    if bwd_ms is not None:
+        result["backward"] = {
+            "note": "gradients of the step's layers (context, not the value); TFLOP/s counts 8 d "
+                    "per visible pair, twice the forward, as GPT.estimate_flops does",
+            "attn_bwd_avg_launch_us": round(1e3 * sum(bwd_ms) / L, 3),
+            "attn_bwd_launch_us": [round(1e3 * t, 3) for t in bwd_ms],
+            "attn_bwd_tflops": round(2 * step_flops / (sum(bwd_ms) * 1e-3) / 1e12, 3),
+            "prologue_bwd_avg_launch_us": round(1e3 * sum(pro_bwd_ms) / L, 3),
+            "prologue_bwd_gbs": round(3 * pro_bytes / 2 * L / (sum(pro_bwd_ms) * 1e-3) / 1e9, 1),
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, cpu_inputs, windows, args.cpu_budget)
     print(json.dumps(result), flush=True)

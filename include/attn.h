@@ -216,6 +216,59 @@ int attn_fwd_qknorm_ex(const void* q, const void* k, const void* v, void* k_work
                        int H_kv, int T, int d, int layout, float eps, int window, int causal,
                        int dtype, void* stream);
 
+/*
+ * Backward pass of attn_fwd / attn_fwd_ex: the gradients of sum(dout * out) with respect to q, k
+ * and v ([HABR] the training step's `loss.backward()` through `CausalSelfAttention.forward`; the
+ * gradients are the exact derivatives of the attn_fwd definition). With c = 1/sqrt(d) and
+ * P_ij = exp(c q_i . k_j - lse_i) on the visible set A(i) (0 elsewhere):
+ *   delta_i = dout_i . out_i
+ *   dv_j = sum_i P_ij dout_i
+ *   dS_ij = P_ij (dout_i . v_j - delta_i)
+ *   dq_i = c sum_j dS_ij k_j,    dk_j = c sum_i dS_ij q_i
+ * With H_kv < H a kv head's dk, dv sum over the query heads of its group.
+ *   q, k, v, out, lse   what attn_fwd(_ex) was given and returned (lse is required here)
+ *   dout                DEVICE, q's shape and dtype: the gradient of out
+ *   delta               DEVICE fp32 [B][H][T], written (a by-product the caller allocates)
+ *   dq                  DEVICE, q's shape and dtype, written
+ *   dk, dv              DEVICE, k's shape and dtype, written
+ *   window, causal, B, H, H_kv, T, d, layout, dtype   as in attn_fwd_ex (attn_bwd: H_kv = H,
+ *                       ATTN_LAYOUT_BHTD)
+ * No output (dq, dk, dv, delta) may overlap an input or another output (ATTN_ERR_ALIAS).
+ * bf16: S, dP and the four products run on bf16 MFMA with fp32 accumulation; P and dS are
+ * recomputed in fp32 and rounded to bf16 (nearest even) for the products; dq, dk, dv are rounded
+ * to bf16 once. f32: every step in fp32. Deterministic: no atomics, fixed summation order.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int T,
+             int d, int window, int causal, int dtype, void* stream);
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
+                int H_kv, int T, int d, int layout, int window, int causal, int dtype,
+                void* stream);
+
+/*
+ * Backward of attn_qknorm_rope(_ex) ([HABR] `norm` and `apply_rotary_emb`): for each raw row x
+ * with r = 1/sqrt(mean_j x_j^2 + eps) and x^ = r x, given dy (the gradient of the normalised,
+ * rotated row), g = the rotation of dy by the opposite angle
+ *   g_j = dy_j cos[t][j] - dy_{j+h} sin[t][j],   g_{j+h} = dy_j sin[t][j] + dy_{j+h} cos[t][j]
+ * and dx = r (g - x^ mean_j(g_j x^_j)).
+ *   q, k            DEVICE, the raw rows the forward prologue was given (read)
+ *   dq_in, dk_in    DEVICE, gradients of the prologue's outputs (read)
+ *   dq_out, dk_out  DEVICE, gradients of q and k (written); dq_out may equal dq_in and dk_out
+ *                   dk_in (in place); any other overlap is ATTN_ERR_ALIAS
+ *   q, dq_in and dq_out may all be NULL: then only k's rows are processed (some but not all of
+ *   them NULL is ATTN_ERR_NULL)
+ *   cos_tab, sin_tab, eps, d, dtype and the shape arguments as in attn_qknorm_rope(_ex)
+ * Arithmetic is fp32; bf16 outputs are rounded to nearest even.
+ */
+int attn_qknorm_rope_bwd(const void* q, const void* k, const void* dq_in, const void* dk_in,
+                         void* dq_out, void* dk_out, const float* cos_tab, const float* sin_tab,
+                         int B, int H, int T, int d, float eps, int dtype, void* stream);
+int attn_qknorm_rope_bwd_ex(const void* q, const void* k, const void* dq_in, const void* dk_in,
+                            void* dq_out, void* dk_out, const float* cos_tab,
+                            const float* sin_tab, int B, int H, int H_kv, int T, int d,
+                            int layout, float eps, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -397,3 +397,93 @@ def test_row_width_limit(lib):
     assert _qkn_ex(lib, a) == _lib.ATTN_ERR_SHAPE
     a["H"] = a["H_kv"] = (1 << 18) - 1  # just below: reaches the eps rule
     assert _qkn_ex(lib, a) == _lib.ATTN_ERR_ARG
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward entry points.
+# ---------------------------------------------------------------------------------------------
+
+_BW = {n: (i + 1) * P for i, n in enumerate(("q", "k", "v", "out", "do", "lse", "delta", "dq",
+                                              "dk", "dv"))}
+
+
+def _bwd(lib, **kw):
+    a = dict(_BW, B=1, H=2, H_kv=2, T=64, d=64, layout=0, window=-1, causal=1,
+             dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_bwd_ex(a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], a["delta"],
+                           a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["H_kv"], a["T"], a["d"],
+                           a["layout"], a["window"], a["causal"], a["dtype"], None)
+
+
+BWD_CASES = [
+    ("null lse", dict(lse=None), _lib.ATTN_ERR_NULL),
+    ("null delta", dict(delta=None), _lib.ATTN_ERR_NULL),
+    ("null dv", dict(dv=None), _lib.ATTN_ERR_NULL),
+    ("dtype 2", dict(dtype=2), _lib.ATTN_ERR_DTYPE),
+    ("bf16 d=16", dict(d=16), _lib.ATTN_ERR_HEAD_DIM),
+    ("f32 d=48", dict(d=48, dtype=_lib.ATTN_F32), _lib.ATTN_ERR_HEAD_DIM),
+    ("H_kv=3", dict(H=4, H_kv=3), _lib.ATTN_ERR_SHAPE),
+    ("layout 7", dict(layout=7), _lib.ATTN_ERR_ARG),
+    ("noncausal window", dict(causal=0, window=1), _lib.ATTN_ERR_WINDOW),
+    ("misaligned dk", dict(dk=_BW["dk"] + 8), _lib.ATTN_ERR_ALIGN),
+    ("misaligned delta", dict(delta=_BW["delta"] + 2), _lib.ATTN_ERR_ALIGN),
+    ("dq is q", dict(dq=_BW["q"]), _lib.ATTN_ERR_ALIAS),
+    ("dv inside dout", dict(dv=_BW["do"] + 64), _lib.ATTN_ERR_ALIAS),
+    ("dk is dv", dict(dk=_BW["dv"]), _lib.ATTN_ERR_ALIAS),
+    ("delta inside lse", dict(delta=_BW["lse"] + 4), _lib.ATTN_ERR_ALIAS),
+    ("delta inside dq", dict(delta=_BW["dq"] + 256), _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_attn_bwd_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _bwd(lib, **kw) == code, name
+
+
+@no_gpu
+def test_attn_bwd_matches_attn_bwd_ex(lib):
+    for name, kw, code in BWD_CASES:
+        if "H_kv" in kw or "layout" in kw:
+            continue
+        a = dict(_BW, B=1, H=2, T=64, d=64, window=-1, causal=1, dtype=_lib.ATTN_BF16)
+        a.update(kw)
+        rc = lib.attn_bwd(a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], a["delta"], a["dq"],
+                          a["dk"], a["dv"], a["B"], a["H"], a["T"], a["d"], a["window"],
+                          a["causal"], a["dtype"], None)
+        assert rc == code, name
+
+
+_PB = {n: (i + 1) * P for i, n in enumerate(("q", "k", "gq", "gk", "oq", "ok", "cos", "sin"))}
+
+
+def _pbwd(lib, **kw):
+    a = dict(_PB, B=1, H=2, H_kv=2, T=64, d=64, layout=0, eps=1e-6, dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_qknorm_rope_bwd_ex(a["q"], a["k"], a["gq"], a["gk"], a["oq"], a["ok"],
+                                       a["cos"], a["sin"], a["B"], a["H"], a["H_kv"], a["T"],
+                                       a["d"], a["layout"], a["eps"], a["dtype"], None)
+
+
+PBWD_CASES = [
+    ("null k", dict(k=None), _lib.ATTN_ERR_NULL),
+    ("q without dq_in", dict(gq=None), _lib.ATTN_ERR_NULL),
+    ("q without dq_out", dict(oq=None), _lib.ATTN_ERR_NULL),
+    ("dq_in without q", dict(q=None, oq=None), _lib.ATTN_ERR_NULL),
+    ("d=24", dict(d=24), _lib.ATTN_ERR_HEAD_DIM),
+    ("eps < 0", dict(eps=-1.0), _lib.ATTN_ERR_ARG),
+    ("misaligned dk_out", dict(ok=_PB["ok"] + 4), _lib.ATTN_ERR_ALIGN),
+    ("dk_out inside dk_in", dict(ok=_PB["gk"] + 16), _lib.ATTN_ERR_ALIAS),
+    ("dk_out is k", dict(ok=_PB["k"]), _lib.ATTN_ERR_ALIAS),
+    ("dq_out is dk_in", dict(oq=_PB["gk"]), _lib.ATTN_ERR_ALIAS),
+    ("dq_out is q", dict(oq=_PB["q"]), _lib.ATTN_ERR_ALIAS),
+    ("k only, dk_out inside k", dict(q=None, gq=None, oq=None, ok=_PB["k"] + 32),
+     _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", PBWD_CASES, ids=[c[0] for c in PBWD_CASES])
+def test_qknorm_rope_bwd_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _pbwd(lib, **kw) == code, name

@@ -44,6 +44,10 @@ SIGNATURES = {
     "attn_fwd_qknorm_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
                                    c_float, c_int, c_int, c_int, c_void_p]),
+    "attn_bwd": (c_int, [c_void_p] * 10 + [c_int] * 7 + [c_void_p]),
+    "attn_bwd_ex": (c_int, [c_void_p] * 10 + [c_int] * 9 + [c_void_p]),
+    "attn_qknorm_rope_bwd": (c_int, [c_void_p] * 8 + [c_int] * 4 + [c_float, c_int, c_void_p]),
+    "attn_qknorm_rope_bwd_ex": (c_int, [c_void_p] * 8 + [c_int] * 6 + [c_float, c_int, c_void_p]),
 }
 
 # storage orders (attn_layout)

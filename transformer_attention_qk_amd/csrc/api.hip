@@ -280,4 +280,97 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, v
                             ATTN_LAYOUT_BHTD, eps, window, causal, dtype, stream);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Backward pass.
+// ---------------------------------------------------------------------------------------------
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
+                int H_kv, int T, int d, int layout, int window, int causal, int dtype,
+                void* stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !delta || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (dtype == ATTN_BF16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_dims(B, H, H_kv, T, d, layout, &dm, &n_q, &n_kv)) return rc;
+  if (causal != 0 && causal != 1) return ATTN_ERR_WINDOW;
+  if (window < -1 || (causal == 0 && window != -1)) return ATTN_ERR_WINDOW;
+  const void* tens[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* t : tens)
+    if (!aligned16(t)) return ATTN_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return ATTN_ERR_ALIGN;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t qb = n_q * eb, kb = n_kv * eb, lb = (int64_t)B * H * T * 4;
+  // Outputs (dq, dk, dv, delta) overlap no input and no other output.
+  const void* in_p[] = {q, k, v, out, dout, lse};
+  const int64_t in_n[] = {qb, kb, kb, qb, qb, lb};
+  const void* out_p[] = {dq, dk, dv, delta};
+  const int64_t out_n[] = {qb, kb, kb, lb};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(out_p[o], out_n[o], in_p[i], in_n[i])) return ATTN_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlap(out_p[o], out_n[o], out_p[o2], out_n[o2])) return ATTN_ERR_ALIAS;
+  }
+  if (dtype == ATTN_BF16 && !slab_fits(dm)) return ATTN_ERR_SHAPE;
+  const int64_t bh = (int64_t)B * H;
+  if (bh * ((T + 127) / 128) > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (dtype == ATTN_F32 && bh * T * (d / 16) > kMaxGrid) return ATTN_ERR_SHAPE;
+  const hipError_t e = attn::launch_attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, dm,
+                                             window, causal, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int T,
+             int d, int window, int causal, int dtype, void* stream) {
+  return attn_bwd_ex(q, k, v, out, dout, lse, delta, dq, dk, dv, B, H, H, T, d, ATTN_LAYOUT_BHTD,
+                     window, causal, dtype, stream);
+}
+
+int attn_qknorm_rope_bwd_ex(const void* q, const void* k, const void* dq_in, const void* dk_in,
+                            void* dq_out, void* dk_out, const float* cos_tab,
+                            const float* sin_tab, int B, int H, int H_kv, int T, int d,
+                            int layout, float eps, int dtype, void* stream) {
+  // q, dq_in and dq_out are all given or all NULL (then only k's rows are processed).
+  const bool has_q = q != nullptr;
+  if (!k || !dk_in || !dk_out || !cos_tab || !sin_tab || (dq_in != nullptr) != has_q ||
+      (dq_out != nullptr) != has_q)
+    return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_dims(B, H, H_kv, T, d, layout, &dm, &n_q, &n_kv)) return rc;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return ATTN_ERR_ARG;
+  if (2 * (int64_t)B * H > 0x7fffffff) return ATTN_ERR_SHAPE;
+  if (!aligned16(k) || !aligned16(dk_in) || !aligned16(dk_out) || !aligned16(cos_tab) ||
+      !aligned16(sin_tab) || (has_q && (!aligned16(q) || !aligned16(dq_in) || !aligned16(dq_out))))
+    return ATTN_ERR_ALIGN;
+  const int64_t eb = elem_bytes(dtype), qb = n_q * eb, kb = n_kv * eb;
+  // Each output may be its own gradient input (in place) and overlaps nothing else.
+  if (dk_out != dk_in && overlap(dk_out, kb, dk_in, kb)) return ATTN_ERR_ALIAS;
+  if (overlap(dk_out, kb, k, kb)) return ATTN_ERR_ALIAS;
+  if (has_q) {
+    if (dq_out != dq_in && overlap(dq_out, qb, dq_in, qb)) return ATTN_ERR_ALIAS;
+    if (overlap(dq_out, qb, q, qb) || overlap(dq_out, qb, k, kb) || overlap(dq_out, qb, dk_in, kb) ||
+        overlap(dq_out, qb, dk_out, kb) || overlap(dk_out, kb, q, qb) ||
+        overlap(dk_out, kb, dq_in, qb))
+      return ATTN_ERR_ALIAS;
+  }
+  const hipError_t e = attn::launch_qknorm_rope_bwd(q, k, dq_in, dk_in, dq_out, dk_out, cos_tab,
+                                                    sin_tab, dm, eps, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_qknorm_rope_bwd(const void* q, const void* k, const void* dq_in, const void* dk_in,
+                         void* dq_out, void* dk_out, const float* cos_tab, const float* sin_tab,
+                         int B, int H, int T, int d, float eps, int dtype, void* stream) {
+  return attn_qknorm_rope_bwd_ex(q, k, dq_in, dk_in, dq_out, dk_out, cos_tab, sin_tab, B, H, H, T,
+                                 d, ATTN_LAYOUT_BHTD, eps, dtype, stream);
+}
+
 }  // extern "C"

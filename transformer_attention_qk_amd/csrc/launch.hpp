@@ -74,4 +74,19 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
                                float* lse, const Dims& dm, int window, int causal,
                                hipStream_t stream);
 
+// Backward of the QK-norm + RoPE prologue: dq_out, dk_out from the raw rows q, k and the
+// gradients dq_in, dk_in of the prologue's outputs (outputs may equal the inputs' gradients).
+// q == nullptr: k rows only.
+hipError_t launch_qknorm_rope_bwd(const void* q, const void* k, const void* dq_in,
+                                  const void* dk_in, void* dq_out, void* dk_out,
+                                  const float* cos_tab, const float* sin_tab, const Dims& dm,
+                                  float eps, int dtype, hipStream_t stream);
+
+// Attention backward: delta (fp32 [B][H][T]) = rowsum(dout * out), then dq, dk, dv.
+// bf16: d in {32, 64, 128}; f32: d in {16, 32, 64, 128}.
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, float* delta, void* dq, void* dk,
+                           void* dv, const Dims& dm, int window, int causal, int dtype,
+                           hipStream_t stream);
+
 }  // namespace attn

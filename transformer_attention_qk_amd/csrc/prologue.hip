@@ -167,6 +167,131 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   }
 }
 
+// Backward of the prologue for the same rows: given the raw row x and the gradient dy of
+// y = RoPE(RMSNorm(x)), dx = r (g - xh mean(g xh)) with r = (mean(x^2) + eps)^(-1/2), xh = r x
+// and g the rotation of dy by the opposite angles (g_j = dy_j cos + dy_{j+h} (-sin) in the first
+// half, g_{j+h} = dy_j sin + dy_{j+h} cos in the second): the chain rule of `norm` and
+// `apply_rotary_emb`. Same row grouping as the forward; dx may be dy itself (each lane reads its
+// chunks of the row, and the partner's through a shuffle, before any lane of the row stores).
+template <typename Elem, int D>
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
+    const Elem* __restrict__ q, const Elem* __restrict__ k, const Elem* dq_in, const Elem* dk_in,
+    Elem* dq_out, Elem* dk_out, const float* __restrict__ cos_tab,
+    const float* __restrict__ sin_tab, Strides sq, Strides sk, FastDiv H, FastDiv H_kv,
+    int heads_q, int heads, int T, FastDiv t_blocks, float eps) {
+  constexpr int E = kE<Elem>;
+  constexpr int HALF = D / 2;
+  constexpr int L = D / E;
+  constexpr int TPB = 256 / L;
+  const int h = (int)t_blocks.div(blockIdx.x);  // block-uniform
+  const int tb = (int)blockIdx.x - h * (int)t_blocks.d;
+  const int t_loc = (int)threadIdx.x / L;
+  const int t0 = tb * TPB;
+  const bool valid = t0 + t_loc < T;
+  const int t = valid ? t0 + t_loc : T - 1;
+  const int r_loc = t - t0;
+  const int sub = (int)threadIdx.x % L;
+  const bool first = sub < L / 2;
+  const int j0 = (sub % (L / 2)) * E;
+  int64_t base;
+  int lane_off;
+  if (h < heads_q) {
+    const uint32_t b = H.div((uint32_t)h);
+    base = (int64_t)b * sq.b + (int64_t)(h - b * H.d) * sq.h + (int64_t)t0 * sq.t;
+    lane_off = r_loc * sq.t + sub * E;
+  } else {
+    const uint32_t hk = (uint32_t)(h - heads_q), b = H_kv.div(hk);
+    base = (int64_t)b * sk.b + (int64_t)(hk - b * H_kv.d) * sk.h + (int64_t)t0 * sk.t;
+    lane_off = r_loc * sk.t + sub * E;
+  }
+  const bool isq = h < heads_q;
+  const int64_t off = base + lane_off;
+  const u32x4 xraw = *reinterpret_cast<const u32x4*>((isq ? q : k) + off);
+  const u32x4 graw = *reinterpret_cast<const u32x4*>((isq ? dq_in : dk_in) + off);
+  float c[E], s[E];
+  const float* ct = cos_tab + (int64_t)t * HALF + j0;
+  const float* st = sin_tab + (int64_t)t * HALF + j0;
+#pragma unroll
+  for (int i = 0; i < E; i += 4) {
+    Vec<float, 4>::load(ct + i, c + i);
+    Vec<float, 4>::load(st + i, s + i);
+  }
+  u32x4 gpart;
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) gpart[wd] = (uint32_t)__shfl_xor((int)graw[wd], L / 2);
+  float x[E], dy[E], dyp[E];
+  Vec<Elem, E>::load(reinterpret_cast<const Elem*>(&xraw), x);
+  Vec<Elem, E>::load(reinterpret_cast<const Elem*>(&graw), dy);
+  Vec<Elem, E>::load(reinterpret_cast<const Elem*>(&gpart), dyp);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+  float g[E], xh[E], gx = 0.f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    // first half: dy_j cos - dy_{j+h} sin; second half: dy_j sin + dy_{j+h} cos (own = dy of
+    // this lane's element, partner = the other half's)
+    g[i] = first ? fmaf(dy[i], c[i], -(dyp[i] * s[i])) : fmaf(dy[i], c[i], dyp[i] * s[i]);
+    xh[i] = x[i] * rinv;
+    gx = fmaf(g[i], xh[i], gx);
+  }
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) gx += __shfl_xor(gx, o);
+  const float mgx = gx * (1.0f / D);
+  float dx[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) dx[i] = rinv * fmaf(-xh[i], mgx, g[i]);
+  if (valid) Vec<Elem, E>::store((isq ? dq_out : dk_out) + off, dx);
+}
+
+template <typename Elem, int D>
+static hipError_t launch_qknorm_rope_bwd_t(const void* q, const void* k, const void* dq_in,
+                                           const void* dk_in, void* dq_out, void* dk_out,
+                                           const float* cos_tab, const float* sin_tab,
+                                           const Dims& dm, float eps, hipStream_t stream) {
+  constexpr int L = D / kE<Elem>;
+  constexpr int TPB = 256 / L;
+  const int T = dm.T;
+  const Geometry geo = make_geometry(dm);
+  const int heads = dm.B * dm.H_kv;
+  const int heads_q = (q != nullptr) ? dm.B * dm.H : 0;
+  const int t_blocks = (T + TPB - 1) / TPB;
+  const int64_t grid = (int64_t)t_blocks * (heads_q + heads);
+  hipLaunchKernelGGL((qknorm_rope_bwd_kernel<Elem, D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const Elem*)q, (const Elem*)k, (const Elem*)dq_in, (const Elem*)dk_in,
+                     (Elem*)dq_out, (Elem*)dk_out, cos_tab, sin_tab, geo.q, geo.kv,
+                     make_fastdiv((uint32_t)dm.H), make_fastdiv((uint32_t)dm.H_kv), heads_q,
+                     heads, T, make_fastdiv((uint32_t)t_blocks), eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope_bwd(const void* q, const void* k, const void* dq_in,
+                                  const void* dk_in, void* dq_out, void* dk_out,
+                                  const float* cos_tab, const float* sin_tab, const Dims& dm,
+                                  float eps, int dtype, hipStream_t stream) {
+  const int d = dm.d;
+#define ATTN_QKNB_CASE(ELEM, DD)                                                                \
+  if (d == DD)                                                                                  \
+    return launch_qknorm_rope_bwd_t<ELEM, DD>(q, k, dq_in, dk_in, dq_out, dk_out, cos_tab,      \
+                                              sin_tab, dm, eps, stream);
+  if (dtype == 0) {
+    ATTN_QKNB_CASE(bf16, 16)
+    ATTN_QKNB_CASE(bf16, 32)
+    ATTN_QKNB_CASE(bf16, 64)
+    ATTN_QKNB_CASE(bf16, 128)
+  } else {
+    ATTN_QKNB_CASE(float, 16)
+    ATTN_QKNB_CASE(float, 32)
+    ATTN_QKNB_CASE(float, 64)
+    ATTN_QKNB_CASE(float, 128)
+  }
+#undef ATTN_QKNB_CASE
+  return hipErrorInvalidValue;
+}
+
 template <typename Elem, int D>
 static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out, void* k_out,
                                        const float* cos_tab, const float* sin_tab, const Dims& dm,

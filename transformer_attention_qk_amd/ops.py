@@ -208,3 +208,82 @@ def attention_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torc
     (two calls: attn_qknorm_rope_ex writes the normalised q and k, attn_fwd_ex reads them)."""
     qn, kn = qknorm_rope(q, k, cos, sin, eps, qn, kn, layout=layout)
     return attn_fwd(qn, kn, v, window=window, causal=True, out=out, lse=lse, layout=layout)
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+             lse: torch.Tensor, dout: torch.Tensor, window: int = -1, causal: bool = True,
+             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+             dv: torch.Tensor | None = None, delta: torch.Tensor | None = None,
+             layout: str = "bhtd"):
+    """Gradients (dq, dk, dv) of sum(dout * out) for (out, lse) = attn_fwd(q, k, v, window,
+    causal, layout=layout). ``delta`` (fp32 [B, H, T], rowsum(dout * out)) is a by-product."""
+    lib = _lib.load()
+    _require(q, "q")
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bf16 or fp32")
+    _require(k, "k", dtype=q.dtype)
+    B, H, H_kv, T, d = _geometry(q, k, layout)
+    _require(v, "v", k.shape, q.dtype)
+    _require(out, "out", q.shape, q.dtype)
+    _require(dout, "dout", q.shape, q.dtype)
+    _require(lse, "lse", (B, H, T), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if delta is None else delta
+    _require(dq, "dq", q.shape, q.dtype)
+    _require(dk, "dk", k.shape, q.dtype)
+    _require(dv, "dv", k.shape, q.dtype)
+    _require(delta, "delta", (B, H, T), torch.float32)
+    rc = lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta),
+                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, H_kv, T, d, _LAYOUTS[layout],
+                         int(window), int(bool(causal)), _DTYPES[q.dtype], _stream_handle())
+    _lib.check("attn_bwd_ex", rc)
+    return dq, dk, dv
+
+
+def qknorm_rope_bwd(q: torch.Tensor | None, k: torch.Tensor, dq_in: torch.Tensor | None,
+                    dk_in: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, eps: float = 1e-6,
+                    dq_out: torch.Tensor | None = None, dk_out: torch.Tensor | None = None,
+                    layout: str = "bhtd"):
+    """Gradients of the raw q, k of qknorm_rope given the gradients of its outputs; outputs may
+    be dq_in, dk_in themselves (in place). With q None only k is processed."""
+    lib = _lib.load()
+    _require(k, "k")
+    if k.dtype not in _DTYPES:
+        raise ValueError("k must be bf16 or fp32")
+    if (q is None) != (dq_in is None):
+        raise ValueError("q and dq_in are given together")
+    if q is not None:
+        _require(q, "q", dtype=k.dtype)
+    B, H, H_kv, T, d = _geometry(q, k, layout)
+    _rope_tables(cos, sin, T, d)
+    _require(dk_in, "dk_in", k.shape, k.dtype)
+    dk_out = torch.empty_like(k) if dk_out is None else dk_out
+    _require(dk_out, "dk_out", k.shape, k.dtype)
+    if q is not None:
+        _require(dq_in, "dq_in", q.shape, q.dtype)
+        dq_out = torch.empty_like(q) if dq_out is None else dq_out
+        _require(dq_out, "dq_out", q.shape, q.dtype)
+    else:
+        dq_out = None
+    rc = lib.attn_qknorm_rope_bwd_ex(_ptr(q), _ptr(k), _ptr(dq_in), _ptr(dk_in), _ptr(dq_out),
+                                     _ptr(dk_out), _ptr(cos), _ptr(sin), B, H, H_kv, T, d,
+                                     _LAYOUTS[layout], float(eps), _DTYPES[k.dtype],
+                                     _stream_handle())
+    _lib.check("attn_qknorm_rope_bwd_ex", rc)
+    return dq_out, dk_out
+
+
+def attention_layer_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                             cos: torch.Tensor, sin: torch.Tensor, window: int = -1,
+                             eps: float = 1e-6, layout: str = "bhtd"):
+    """Gradients (dq, dk, dv) with respect to the raw q, k, v of one attention layer
+    (attention_layer or attn_fwd_qknorm, whose out and lse are passed in): the normalised,
+    rotated q and k are recomputed (attn_qknorm_rope_ex), attn_bwd_ex runs on them, and
+    attn_qknorm_rope_bwd_ex turns their gradients into those of the raw rows, in place."""
+    qn, kn = qknorm_rope(q, k, cos, sin, eps, layout=layout)
+    dqn, dkn, dv = attn_bwd(qn, kn, v, out, lse, dout, window=window, causal=True, layout=layout)
+    dq, dk = qknorm_rope_bwd(q, k, dqn, dkn, cos, sin, eps, dq_out=dqn, dk_out=dkn, layout=layout)
+    return dq, dk, dv
