@@ -9,6 +9,7 @@ from .attention import (  # noqa: F401
     ROPE_BASE_DEFAULT,
     attention,
     attention_layer,
+    decode_attention,
     kv_head,
     qknorm_rope,
     rms_norm,

@@ -217,3 +217,42 @@ def attention_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int = -
     """
     qn, kn = qknorm_rope(q, k, eps, base)
     return attention(qn, kn, v, window, causal, rows=rows)
+
+
+def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                     lengths=None, window: int = -1) -> tuple[np.ndarray, np.ndarray]:
+    """One generation step: the newest token's query against the cached keys and values, fp64.
+
+    q: [B, H, d] (the query of the token at position n_b - 1); k_cache, v_cache: [B, H_kv, S, d]
+    with H_kv dividing H (R13); lengths: n_b per batch (1 <= n_b <= S; None means S). Returns
+    (O [B, H, d], LSE [B, H]).
+
+    [GEOM] "A Máscara Causal": training and inference are the same forward pass, so the newest
+    token attends exactly as the last row of the causal attention does: to the tokens 0..n-1,
+    cut to n - 1 - j <= window when window >= 0 (R4). [CNOYU]/[HABR] generation appends one
+    token at a time ("O Que um Modelo de Linguagem Prevê": autoregressive generation).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k_cache, dtype=np.float64)
+    v = np.asarray(v_cache, dtype=np.float64)
+    B, H, d = q.shape
+    H_kv, S = k.shape[1], k.shape[2]
+    if k.shape != (B, H_kv, S, d) or v.shape[:3] != (B, H_kv, S):
+        raise ValueError("k_cache, v_cache must be [B, H_kv, S, d] with q [B, H, d]")
+    lengths = [S] * B if lengths is None else [int(n) for n in lengths]
+    if any(n < 1 or n > S for n in lengths):
+        raise ValueError("lengths must lie in [1, S]")
+    out = np.zeros((B, H, v.shape[-1]))
+    lse = np.zeros((B, H))
+    scale = 1.0 / math.sqrt(d)
+    for b in range(B):
+        n = lengths[b]
+        lo = 0 if window < 0 else max(0, n - 1 - window)
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            s = (k[b, g, lo:n] @ q[b, h]) * scale
+            m = np.max(s)
+            row_lse = m + np.log(np.sum(np.exp(s - m)))
+            out[b, h] = np.exp(s - row_lse) @ v[b, g, lo:n]
+            lse[b, h] = row_lse
+    return out, lse

@@ -484,6 +484,52 @@ def check_backward_invariants(o, seed=14):
     assert np.allclose(o.rope_apply_backward(o.rope_apply(gy, cos, sin), cos, sin), gy, atol=1e-13)
 
 
+def check_decode(o, seed=15):
+    """decode_attention against brute force with math.fsum, torch's scaled_dot_product_attention
+    on the one query row, the zero-query closed form (uniform weights over the visible keys),
+    and the last row of the (independently pinned) causal attention over the whole prefix."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(seed)
+    B, H, H_kv, S, d = 3, 4, 2, 9, 4
+    q = rng.standard_normal((B, H, d))
+    k = rng.standard_normal((B, H_kv, S, d))
+    v = rng.standard_normal((B, H_kv, S, d))
+    lengths = [1, 5, 9]
+    for window in (-1, 0, 2, 20):
+        out, lse = o.decode_attention(q, k, v, lengths, window)
+        for b, n in enumerate(lengths):
+            lo = 0 if window < 0 else max(0, n - 1 - window)
+            for h in range(H):
+                g = h // (H // H_kv)
+                s = [math.fsum(q[b, h, c] * k[b, g, j, c] for c in range(d)) / math.sqrt(d)
+                     for j in range(lo, n)]
+                m = max(s)
+                ll = m + math.log(math.fsum(math.exp(x - m) for x in s))
+                assert abs(lse[b, h] - ll) < 1e-12
+                for c in range(d):
+                    ref = math.fsum(math.exp(s[i] - ll) * v[b, g, lo + i, c] for i in range(len(s)))
+                    assert abs(out[b, h, c] - ref) < 1e-12
+                ts = F.scaled_dot_product_attention(
+                    torch.tensor(q[b, h][None, None, None]), torch.tensor(k[b, g, lo:n][None, None]),
+                    torch.tensor(v[b, g, lo:n][None, None]))
+                assert np.allclose(ts.numpy()[0, 0, 0], out[b, h], rtol=0, atol=1e-12)
+    out, lse = o.decode_attention(np.zeros_like(q), k, v, lengths, 3)
+    for b, n in enumerate(lengths):
+        lo = max(0, n - 4)
+        for h in range(H):
+            g = h // (H // H_kv)
+            assert np.allclose(out[b, h], v[b, g, lo:n].mean(axis=0), atol=1e-13)
+            assert abs(lse[b, h] - math.log(n - lo)) < 1e-13
+    # the newest token's row of the causal attention over the prefix
+    for n, window in ((9, -1), (7, 3)):
+        qs = rng.standard_normal((1, H, n, d))
+        ro, rl = o.attention(qs, k[:1, :, :n], v[:1, :, :n], window=window)
+        out, lse = o.decode_attention(qs[:, :, n - 1], k[:1], v[:1], [n], window)
+        assert np.allclose(out, ro[:, :, n - 1], atol=1e-13) and np.allclose(lse, rl[:, :, n - 1], atol=1e-13)
+
+
 BACKWARD_CHECKS = [
     check_backward_finite_differences,
     check_layer_backward_finite_differences,
@@ -508,4 +554,5 @@ ALL_CHECKS = [
     check_norm_rope_commute,
     check_sssl_windows,
     check_gqa_head_mapping,
+    check_decode,
 ] + BACKWARD_CHECKS

@@ -219,3 +219,36 @@ def test_prologue_backward_mutations_are_caught(name, fn):
                 rms_norm_backward=oracle.rms_norm_backward,
                 rope_apply_backward=oracle.rope_apply_backward)
     assert _fails(o, BWD_CHECKS), name
+
+
+def _decode_with(lo_fn=None, hi_off=0, kv_map=None):
+    def dec(q, k, v, lengths=None, window=-1):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        B, H, d = q.shape
+        H_kv, S = k.shape[1], k.shape[2]
+        lengths = [S] * B if lengths is None else list(lengths)
+        out, lse = np.zeros((B, H, v.shape[-1])), np.zeros((B, H))
+        for b in range(B):
+            n = lengths[b]
+            lo = lo_fn(n, window) if lo_fn else (0 if window < 0 else max(0, n - 1 - window))
+            hi = max(lo + 1, n + hi_off)
+            for h in range(H):
+                g = kv_map(h, H, H_kv) if kv_map else h // (H // H_kv)
+                s = k[b, g, lo:hi] @ q[b, h] / math.sqrt(d)
+                l = s.max() + np.log(np.exp(s - s.max()).sum())
+                out[b, h], lse[b, h] = np.exp(s - l) @ v[b, g, lo:hi], l
+        return out, lse
+    return dec
+
+
+def test_unmutated_decode_copy_passes():
+    assert not _fails(_mutant(decode_attention=_decode_with()), [pins.check_decode])
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("window one key short", dict(lo_fn=lambda n, w: 0 if w < 0 else min(n - 1, max(0, n - w)))),
+    ("newest key left out", dict(hi_off=-1)),
+    ("kv heads interleaved", dict(kv_map=lambda h, H, H_kv: h % H_kv)),
+])
+def test_decode_mutations_are_caught(name, kw):
+    assert _fails(_mutant(decode_attention=_decode_with(**kw)), [pins.check_decode]), name
