@@ -140,7 +140,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3)")
     ap.add_argument("--workload", default="andrea120m_sssl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward and decode timings")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue"],
                     default=None)
@@ -335,6 +335,32 @@ def main() -> int:
     ms_per_step_unfused = time_steps(step_unfused)
     pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
 
+    # Decode (context): one generation step against each layer's keys and values as the cache.
+    dec_ms = None
+    if not args.no_backward:
+        qdec = [qn[l][:, :, -1].contiguous() if layout == "bhtd" else qn[l][:, -1].contiguous()
+                for l in range(L)]
+        dout_dec = [torch.empty_like(x) for x in qdec]
+        dlse_dec = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(L)]
+        wsb = [lib.attn_decode_workspace_bytes(B, H, T, d, windows[l]) for l in range(L)]
+        ws_dec = [torch.empty((n // 4 + 4,), dtype=torch.float32, device="cuda") for n in wsb]
+        PD = [tuple(t.data_ptr() for t in (qdec[l], dout_dec[l], dlse_dec[l], ws_dec[l]))
+              for l in range(L)]
+
+        def decode_step(l):
+            _, _, pv, _, pkn, _, _ = P[l]
+            pqd, pod, pld, pws = PD[l]
+            return lib.attn_decode_ex(pqd, pkn, pv, None, pod, pld, pws, wsb[l], B, H, H, T, d,
+                                      lay, windows[l], bf16, stream)
+
+        def nothing(l):
+            return 0
+
+        for l in range(L):
+            _lib.check("decode", decode_step(l))
+        dec_ms, _ = time_launches(decode_step, nothing)
+        dec_bytes = [B * H * (min(T, W + 1 if W >= 0 else T) * 4 * d + 4 * d) for W in windows]
+
     # The backward pass (context, not the value): per layer, the gradient of sum(dout * out)
     # through attn_bwd_ex on the normalised q, k the two-call path wrote (kernels: delta, dK/dV,
     # dQ), then the prologue's backward attn_qknorm_rope_bwd_ex in place.
@@ -436,6 +462,17 @@ def main() -> int:
             "prologue_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
         },
     }
+    if dec_ms is not None:
+        result["decode"] = {
+            "note": "one generation step per layer: the newest token of each (batch, head) "
+                    "against the layer's normalised keys and values as a full cache of T tokens "
+                    "(attn_decode_ex); HBM-bound, bytes = cache rows read + q + out",
+            "avg_launch_us": round(1e3 * sum(dec_ms) / L, 3),
+            "launch_us": [round(1e3 * t, 3) for t in dec_ms],
+            "bytes_per_launch": dec_bytes,
+            "achieved_gbs": round(sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9, 1),
+            "peak_gbs": PEAK_HBM_GBS,
+        }
     if bwd_ms is not None:
         result["backward"] = {
             "note": "gradients of the step's layers (context, not the value); TFLOP/s counts 8 d "

@@ -269,6 +269,39 @@ int attn_qknorm_rope_bwd_ex(const void* q, const void* k, const void* dq_in, con
                             const float* sin_tab, int B, int H, int H_kv, int T, int d,
                             int layout, float eps, int dtype, void* stream);
 
+/*
+ * Decode: one generation step ([GEOM] "A Máscara Causal": inference runs the same masked forward
+ * as training; generation appends one token at a time). For every (batch b, head h) the newest
+ * token's query q[b][h] (already normalised and rotated, like the rows attn_fwd takes) attends
+ * to the cached keys and values of its batch entry, n_b = lengths[b] tokens with its own key and
+ * value at position n_b - 1: keys j with max(0, n_b - 1 - window) <= j < n_b (window = -1: all
+ * n_b), i.e. the last row of attn_fwd over the prefix:
+ *   out[b][h] = sum_j softmax_j(q . k_j / sqrt(d)) v_j,   lse[b][h] = ln sum_j exp(q . k_j / sqrt(d))
+ *   q, out           DEVICE [B][H][d] of dtype (read / written)
+ *   k_cache, v_cache DEVICE [B][H_kv][S][d] (ATTN_LAYOUT_BHTD) or [B][S][H_kv][d]
+ *                    (ATTN_LAYOUT_BTHD) of dtype, S = the cache's capacity; slots past n_b unread
+ *   lengths          DEVICE int32 [B]: n_b, clamped to [1, S] on the device; NULL: every n_b = S
+ *   lse              DEVICE fp32 [B][H], written; may be NULL
+ *   workspace        DEVICE scratch of at least attn_decode_workspace_bytes(B, H, S, d, window)
+ *                    bytes (16-byte aligned), owned by the caller; contents are overwritten and
+ *                    calls that share one workspace must be ordered on one stream
+ *   window           -1 or >= 0 (else ATTN_ERR_WINDOW)
+ *   d, dtype         ATTN_BF16: {32, 64, 128}; ATTN_F32: {16, 32, 64, 128}
+ * Scores, weights and sums are fp32 for both dtypes (the weights are not rounded); out is
+ * rounded once. No written buffer may overlap another argument's buffer (ATTN_ERR_ALIAS); a
+ * workspace below the required size is ATTN_ERR_ARG. attn_decode is attn_decode_ex with
+ * H_kv = H and ATTN_LAYOUT_BHTD.
+ * attn_decode_workspace_bytes returns the size, or -1 for B, H, S < 1, d outside [1, 256] or
+ * window < -1; it is host-only.
+ */
+long long attn_decode_workspace_bytes(int B, int H, int S, int d, int window);
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
+                void* out, float* lse, void* workspace, long long workspace_bytes, int B, int H,
+                int S, int d, int window, int dtype, void* stream);
+int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
+                   void* out, float* lse, void* workspace, long long workspace_bytes, int B,
+                   int H, int H_kv, int S, int d, int layout, int window, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

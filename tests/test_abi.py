@@ -17,7 +17,8 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*\w+\s*\*?\s*(attn_\w+)\s*\(", src,
+                                 flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +29,9 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_qnorm", "attn_fwd_qknorm", "attn_qknorm_rope",
-            "attn_rope_table", "attn_strerror", "attn_sssl_windows", "attn_version"} <= set(names)
+            "attn_rope_table", "attn_strerror", "attn_sssl_windows", "attn_version",
+            "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_qknorm_rope_bwd", "attn_decode",
+            "attn_decode_ex", "attn_decode_workspace_bytes"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -487,3 +490,53 @@ PBWD_CASES = [
 @pytest.mark.parametrize("name,kw,code", PBWD_CASES, ids=[c[0] for c in PBWD_CASES])
 def test_qknorm_rope_bwd_rejects_before_any_hip_call(lib, name, kw, code):
     assert _pbwd(lib, **kw) == code, name
+
+
+# ---------------------------------------------------------------------------------------------
+# Decode.
+# ---------------------------------------------------------------------------------------------
+
+def test_decode_workspace_bytes(lib):
+    # B * H * ceil(keys / 128) * (d + 2) * 4, keys = min(S, window + 1)
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, -1) == 2 * 3 * 8 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, 127) == 2 * 3 * 1 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, 128) == 2 * 3 * 2 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(0, 3, 1000, 64, -1) == -1
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 64, -2) == -1
+
+
+_DC = {n: (i + 1) * P for i, n in enumerate(("q", "k", "v", "len", "out", "lse", "ws"))}
+
+
+def _dec(lib, **kw):
+    a = dict(_DC, wsb=1 << 20, B=2, H=4, H_kv=2, S=300, d=64, layout=0, window=-1,
+             dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_decode_ex(a["q"], a["k"], a["v"], a["len"], a["out"], a["lse"], a["ws"],
+                              a["wsb"], a["B"], a["H"], a["H_kv"], a["S"], a["d"], a["layout"],
+                              a["window"], a["dtype"], None)
+
+
+DEC_CASES = [
+    ("null q", dict(q=None), _lib.ATTN_ERR_NULL),
+    ("null workspace", dict(ws=None), _lib.ATTN_ERR_NULL),
+    ("dtype 5", dict(dtype=5), _lib.ATTN_ERR_DTYPE),
+    ("bf16 d=16", dict(d=16), _lib.ATTN_ERR_HEAD_DIM),
+    ("S=0", dict(S=0), _lib.ATTN_ERR_SHAPE),
+    ("H_kv=3", dict(H_kv=3), _lib.ATTN_ERR_SHAPE),
+    ("layout 3", dict(layout=3), _lib.ATTN_ERR_ARG),
+    ("window -2", dict(window=-2), _lib.ATTN_ERR_WINDOW),
+    ("misaligned out", dict(out=_DC["out"] + 8), _lib.ATTN_ERR_ALIGN),
+    ("misaligned lengths", dict(len=_DC["len"] + 2), _lib.ATTN_ERR_ALIGN),
+    ("workspace too small", dict(wsb=2 * 4 * 3 * 66 * 4 - 4), _lib.ATTN_ERR_ARG),
+    ("out is q", dict(out=_DC["q"]), _lib.ATTN_ERR_ALIAS),
+    ("workspace inside k", dict(ws=_DC["k"] + 4096), _lib.ATTN_ERR_ALIAS),
+    ("lse inside workspace", dict(lse=_DC["ws"] + 16), _lib.ATTN_ERR_ALIAS),
+    ("out over lengths", dict(out=_DC["len"] - 16), _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _dec(lib, **kw) == code, name

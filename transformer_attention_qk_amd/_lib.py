@@ -48,6 +48,9 @@ SIGNATURES = {
     "attn_bwd_ex": (c_int, [c_void_p] * 10 + [c_int] * 9 + [c_void_p]),
     "attn_qknorm_rope_bwd": (c_int, [c_void_p] * 8 + [c_int] * 4 + [c_float, c_int, c_void_p]),
     "attn_qknorm_rope_bwd_ex": (c_int, [c_void_p] * 8 + [c_int] * 6 + [c_float, c_int, c_void_p]),
+    "attn_decode_workspace_bytes": (ctypes.c_longlong, [c_int] * 5),
+    "attn_decode": (c_int, [c_void_p] * 7 + [ctypes.c_longlong] + [c_int] * 6 + [c_void_p]),
+    "attn_decode_ex": (c_int, [c_void_p] * 7 + [ctypes.c_longlong] + [c_int] * 8 + [c_void_p]),
 }
 
 # storage orders (attn_layout)

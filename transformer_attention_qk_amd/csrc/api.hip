@@ -373,4 +373,56 @@ int attn_qknorm_rope_bwd(const void* q, const void* k, const void* dq_in, const 
                                  d, ATTN_LAYOUT_BHTD, eps, dtype, stream);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode.
+// ---------------------------------------------------------------------------------------------
+
+long long attn_decode_workspace_bytes(int B, int H, int S, int d, int window) {
+  if (B < 1 || H < 1 || S < 1 || d < 1 || d > 256 || window < -1) return -1;
+  return (long long)attn::decode_workspace_bytes(B, H, S, d, window);
+}
+
+int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
+                   void* out, float* lse, void* workspace, long long workspace_bytes, int B,
+                   int H, int H_kv, int S, int d, int layout, int window, int dtype,
+                   void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !workspace) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (dtype == ATTN_BF16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_dims(B, H, H_kv, S, d, layout, &dm, &n_q, &n_kv)) return rc;
+  if (window < -1) return ATTN_ERR_WINDOW;
+  const void* vec[] = {q, k_cache, v_cache, out, workspace};
+  for (const void* t : vec)
+    if (!aligned16(t)) return ATTN_ERR_ALIGN;
+  if ((lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGN;
+  const int64_t need = attn::decode_workspace_bytes(B, H, S, d, window);
+  if (workspace_bytes < need) return ATTN_ERR_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t qb = (int64_t)B * H * d * eb, kb = n_kv * eb;
+  // Written: out, lse, workspace; none overlaps another buffer.
+  const void* bufs[] = {q, k_cache, v_cache, lengths, out, lse, workspace};
+  const int64_t len[] = {qb, kb, kb, (int64_t)B * 4, qb, (int64_t)B * H * 4, need};
+  for (int w = 4; w < 7; ++w) {
+    if (!bufs[w]) continue;
+    for (int o = 0; o < 7; ++o)
+      if (o != w && bufs[o] && overlap(bufs[w], len[w], bufs[o], len[o])) return ATTN_ERR_ALIAS;
+  }
+  if ((int64_t)B * H_kv * attn::decode_splits(S, window) > kMaxGrid) return ATTN_ERR_SHAPE;
+  const hipError_t e = attn::launch_attn_decode(q, k_cache, v_cache, lengths, out, lse, workspace,
+                                                dm, window, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
+                void* out, float* lse, void* workspace, long long workspace_bytes, int B, int H,
+                int S, int d, int window, int dtype, void* stream) {
+  return attn_decode_ex(q, k_cache, v_cache, lengths, out, lse, workspace, workspace_bytes, B, H,
+                        H, S, d, ATTN_LAYOUT_BHTD, window, dtype, stream);
+}
+
 }  // extern "C"

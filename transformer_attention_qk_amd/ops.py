@@ -287,3 +287,50 @@ def attention_layer_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dqn, dkn, dv = attn_bwd(qn, kn, v, out, lse, dout, window=window, causal=True, layout=layout)
     dq, dk = qknorm_rope_bwd(q, k, dqn, dkn, cos, sin, eps, dq_out=dqn, dk_out=dkn, layout=layout)
     return dq, dk, dv
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           lengths: torch.Tensor | None = None, window: int = -1,
+           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+           want_lse: bool = True, workspace: torch.Tensor | None = None, layout: str = "bhtd"):
+    """One generation step: q [B, H, d] (the newest token's normalised, rotated query) against
+    k_cache, v_cache [B, H_kv, S, d] (or [B, S, H_kv, d] with layout "bthd") holding lengths[b]
+    tokens each (int32 [B] on the GPU; None: all S). Returns (out [B, H, d], lse [B, H]).
+    The split-over-keys workspace is allocated here unless given (the library allocates none)."""
+    lib = _lib.load()
+    _require(q, "q")
+    if q.dim() != 3 or q.dtype not in _DTYPES:
+        raise ValueError("q must be [B, H, d] bf16 or fp32")
+    _require(k_cache, "k_cache", dtype=q.dtype)
+    _require(v_cache, "v_cache", k_cache.shape, q.dtype)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be 4-d")
+    B, H, d = q.shape
+    if layout == "bhtd":
+        _, H_kv, S, _ = k_cache.shape
+    elif layout == "bthd":
+        _, S, H_kv, _ = k_cache.shape
+    else:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}, got {layout!r}")
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or H % H_kv:
+        raise ValueError("k_cache must hold the batch, head dim and a kv head count dividing H")
+    if lengths is not None:
+        _require(lengths, "lengths", (B,), torch.int32)
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.shape, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", (B, H), torch.float32)
+    need = lib.attn_decode_workspace_bytes(B, H, S, d, int(window))
+    if need < 0:
+        raise ValueError("invalid decode shape")
+    if workspace is None:
+        workspace = torch.empty(((need + 3) // 4,), dtype=torch.float32, device=q.device)
+    _require(workspace, "workspace")
+    rc = lib.attn_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths), _ptr(out),
+                            _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            B, H, H_kv, S, d, _LAYOUTS[layout], int(window), _DTYPES[q.dtype],
+                            _stream_handle())
+    _lib.check("attn_decode_ex", rc)
+    return out, lse
