@@ -11,6 +11,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // far above any device memory
 constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr int64_t kMaxItems = kMaxGrid;  // work items (workgroups) of one attention launch
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -174,7 +175,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* l
   }
   if (dtype == ATTN_BF16 && !slab_fits(dm)) return ATTN_ERR_SHAPE;
   const int64_t tiles = (dtype == ATTN_BF16) ? (T + 127) / 128 : (T + 63) / 64;
-  if (bh * tiles > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (bh * tiles > kMaxItems) return ATTN_ERR_SHAPE;
   hipError_t e;
   if (dtype == ATTN_BF16)
     e = attn::launch_attn_fwd_bf16(q, k, v, out, lse, dm, window, causal, (hipStream_t)stream);
@@ -220,7 +221,7 @@ int check_qnorm_args(const void* q, const void* k, const void* v, const void* ou
       return ATTN_ERR_ALIAS;
   }
   if (!slab_fits(*dm)) return ATTN_ERR_SHAPE;
-  if (bh * ((T + 127) / 128) > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (bh * ((T + 127) / 128) > kMaxItems) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -317,7 +318,7 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
   }
   if (dtype == ATTN_BF16 && !slab_fits(dm)) return ATTN_ERR_SHAPE;
   const int64_t bh = (int64_t)B * H;
-  if (bh * ((T + 127) / 128) > kMaxGrid) return ATTN_ERR_SHAPE;
+  if (bh * ((T + 127) / 128) > kMaxItems) return ATTN_ERR_SHAPE;
   if (dtype == ATTN_F32 && bh * T * (d / 16) > kMaxGrid) return ATTN_ERR_SHAPE;
   const hipError_t e = attn::launch_attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, dm,
                                              window, causal, dtype, (hipStream_t)stream);

@@ -768,8 +768,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
   const int q_rs = geo.q.t * 2, kv_rs = geo.kv.t * 2;  // row strides in bytes
   WaveTile<D, MODE, QKN> w;
   w.init(T, window, scale_log2, tid, q_rs);
-  const int bh = (int)(blockIdx.x % BH);
-  const int q0 = (nqt - 1 - (int)(blockIdx.x / BH)) * C::BM;  // heaviest query block first
+  // Item order: heads in groups of 32; within a group the query blocks go heaviest first, each
+  // block index for all the group's heads in turn. Workgroup i runs on XCD i % 8 (round-robin
+  // dispatch), so with whole groups of 32 a head's blocks all land on one XCD, and the
+  // workgroups resident at once cover few heads, whose K/V tiles are then read from that XCD's
+  // L2 rather than from HBM.
+  constexpr int kGroup = 32;
+  const int i = (int)blockIdx.x;
+  const int g = i / (kGroup * nqt);
+  const int gsize = min(kGroup, BH - g * kGroup);
+  const int r = i - g * kGroup * nqt;
+  const int bh = g * kGroup + r % gsize;
+  const int q0 = (nqt - 1 - r / gsize) * C::BM;
   const int64_t hoff = geo.q_head(bh), kvoff = geo.kv_head(bh);
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + kvoff, T * kv_rs);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kvoff, T * kv_rs);
