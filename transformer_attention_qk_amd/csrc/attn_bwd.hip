@@ -106,6 +106,17 @@ __device__ __forceinline__ void store_tile(char* tile, const u32x4 (&x)[BwdCfg<D
   }
 }
 
+// Workgroup i of a grid of n_heads * n_blocks: heads in groups of kGroup, and within a group
+// block rank 0 for every head of the group, then rank 1, and so on.
+__device__ __forceinline__ void group_order(int i, int n_heads, int n_blocks, int kGroup,
+                                            int& head, int& rank) {
+  const int g = i / (kGroup * n_blocks);
+  const int gsize = min(kGroup, n_heads - g * kGroup);
+  const int r = i - g * kGroup * n_blocks;
+  head = g * kGroup + r % gsize;
+  rank = r / gsize;
+}
+
 // Register r of a 32x32 accumulator holds row 8 (r / 4) + 4 (lane / 32) + r % 4.
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
@@ -180,7 +191,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, Geometry geo, int H_kv, int T, int window_arg,
-    float scale_log2, float scale, int nkb) {
+    float scale_log2, float scale, int nkb, int group_heads) {
   using C = BwdCfg<D>;
   // Two buffers, each: Q tile, dO tile, then LSE (base 2) and D of its 64 queries.
   constexpr int BUF = 2 * C::TILE_BYTES + 2 * C::TR * 4;
@@ -188,11 +199,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   const int tid = (int)threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Key blocks in order: with a causal mask the first blocks see the most queries, so the
-  // heaviest workgroups start first.
+  // Item order: kv heads in groups of `group_heads`; within a group the key blocks go heaviest
+  // first (with a causal mask the first blocks see the most queries), each block index for all
+  // of the group's heads in turn. Workgroup i runs on XCD i % 8, so with groups of 32 a head's
+  // blocks share one XCD's L2 and the workgroups resident at once read the query tiles of few
+  // heads; when every head's tiles fit in the caches at once the group is all heads (plain
+  // heaviest-first order).
   const int BG = (int)gridDim.x / nkb;
-  const int kblk = (int)blockIdx.x / BG;
-  const int bg = (int)blockIdx.x - kblk * BG;  // b * H_kv + g
+  int kblk, bg;  // bg = b * H_kv + g
+  group_order((int)blockIdx.x, BG, nkb, group_heads, bg, kblk);
   const int b = bg / H_kv, g = bg - b * H_kv;
   const int group = (int)geo.group.d, H = (int)geo.H.d;
   const int k0 = kblk * 128, kw0 = k0 + 32 * wave;
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dQ, Geometry geo, int BH, int T, int window_arg, float scale_log2,
-    float scale, int nqb) {
+    float scale, int nqb, int group_heads) {
   using C = BwdCfg<D>;
   // Two buffers, each: K tile, V tile.
   constexpr int BUF = 2 * C::TILE_BYTES;
@@ -373,8 +388,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   const int tid = (int)threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = nqb - 1 - (int)blockIdx.x / BH;  // heaviest query blocks first
-  const int bh = (int)blockIdx.x % BH;
+  // Same order as the dK/dV kernel, heaviest (last) query blocks first.
+  int qr, bh;
+  group_order((int)blockIdx.x, BH, nqb, group_heads, bh, qr);
+  const int qb = nqb - 1 - qr;
   const int q0 = qb * 128, qw0 = q0 + 32 * wave, qi = qw0 + l32;
   const int q_rs = geo.q.t * 2, kv_rs = geo.kv.t * 2;
   const int64_t qoff = geo.q_head(bh), kvoff = geo.kv_head(bh);
@@ -601,13 +618,15 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
   hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, MODE>), dim3((unsigned)(dm.B * dm.H_kv * nkb)),
                      dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                      (const bf16*)dout, lse, delta, (bf16*)dk, (bf16*)dv, geo, dm.H_kv, dm.T,
-                     window, scale_log2, scale, nkb);
+                     window, scale_log2, scale, nkb,
+                     group_heads(dm.B * dm.H_kv, (int64_t)dm.T * D * 2 * 2));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BH = dm.B * dm.H;
   hipLaunchKernelGGL((attn_bwd_dq_bf16<D, MODE>), dim3((unsigned)(BH * nkb)), dim3(256), 0,
                      stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                     lse, delta, (bf16*)dq, geo, BH, dm.T, window, scale_log2, scale, nkb);
+                     lse, delta, (bf16*)dq, geo, BH, dm.T, window, scale_log2, scale, nkb,
+                     group_heads(BH, (int64_t)dm.T * D * 2 * 2));
   return hipGetLastError();
 }
 

@@ -760,7 +760,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
     const float* __restrict__ sin_tab, float eps, Geometry geo, int BH, int T, int window_arg,
-    float scale_log2, int nqt) {
+    float scale_log2, int nqt, int group_heads) {
   using C = FwdCfg<D>;
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::TILE_LDS];
@@ -768,12 +768,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
   const int q_rs = geo.q.t * 2, kv_rs = geo.kv.t * 2;  // row strides in bytes
   WaveTile<D, MODE, QKN> w;
   w.init(T, window, scale_log2, tid, q_rs);
-  // Item order: heads in groups of 32; within a group the query blocks go heaviest first, each
-  // block index for all the group's heads in turn. Workgroup i runs on XCD i % 8 (round-robin
-  // dispatch), so with whole groups of 32 a head's blocks all land on one XCD, and the
+  // Item order: heads in groups of kGroup; within a group the query blocks go heaviest first,
+  // each block index for all the group's heads in turn. Workgroup i runs on XCD i % 8
+  // (round-robin dispatch), so with groups of 32 a head's blocks all land on one XCD, and the
   // workgroups resident at once cover few heads, whose K/V tiles are then read from that XCD's
-  // L2 rather than from HBM.
-  constexpr int kGroup = 32;
+  // L2 rather than from HBM; when all heads' K/V fit in the caches together the group is every
+  // head (plain heaviest-first order).
+  const int kGroup = group_heads;
   const int i = (int)blockIdx.x;
   const int g = i / (kGroup * nqt);
   const int gsize = min(kGroup, BH - g * kGroup);
@@ -883,7 +884,8 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE, QKN>), dim3((unsigned)n_items), dim3(256), 0,
                        stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out,
-                       a.lse, a.cos_tab, a.sin_tab, a.eps, a.geo, BH, a.T, a.window, scale_log2, nqt);
+                       a.lse, a.cos_tab, a.sin_tab, a.eps, a.geo, BH, a.T, a.window, scale_log2, nqt,
+                       group_heads(BH, (int64_t)a.T * D * 2 * 2));
   }
   return hipGetLastError();
 }

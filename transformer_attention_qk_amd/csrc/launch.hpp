@@ -50,6 +50,14 @@ inline Geometry make_geometry(const Dims& dm) {
 }
 
 
+// Heads per group of the head-grouped work order (see the kernels): all heads when the tiles
+// they stream (bytes_per_head each) fit in the last-level cache together, else 32, so that the
+// workgroups resident at once work on few heads and share their tiles through an XCD's L2.
+inline int group_heads(int n_heads, int64_t bytes_per_head) {
+  constexpr int64_t kCacheBudget = int64_t(128) << 20;  // half of MI355X's 256 MB Infinity Cache
+  return ((int64_t)n_heads * bytes_per_head <= kCacheBudget) ? n_heads : 32;
+}
+
 hipError_t launch_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base,
                              hipStream_t stream);
 
