@@ -193,9 +193,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
     bf16* __restrict__ dK, bf16* __restrict__ dV, Geometry geo, int H_kv, int T, int window_arg,
     float scale_log2, float scale, int nkb, int group_heads) {
   using C = BwdCfg<D>;
-  // Two buffers, each: Q tile, dO tile, then LSE (base 2) and D of its 64 queries.
+  // Buffers, each: Q tile, dO tile, then LSE (base 2) and D of its 64 queries. d <= 64 runs a
+  // software pipeline over three buffers; d = 128 (whose accumulators leave no registers for a
+  // second set of scores) double-buffers.
+  constexpr bool PIPE = D <= 64;
+  constexpr int NBUF = PIPE ? 3 : 2;
   constexpr int BUF = 2 * C::TILE_BYTES + 2 * C::TR * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF];
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   const int tid = (int)threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,83 +277,126 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
       ls[C::TR + tid] = xd;
     }
   };
-  fetch(0);
-  put(0);
-  __syncthreads();
-
-  for (int i = 0; i < n_tiles; ++i) {
-    // Tile i + 1's loads fly while tile i is used; they land in the other buffer, whose last
-    // readers (tile i - 1) passed the barrier that ended the previous step.
-    if (i + 1 < n_tiles) fetch(i + 1);
-    const char* base = smem + (i & 1) * BUF;
-    const char* qtile = base;
-    const char* dotile = base + C::TILE_BYTES;
-    const float* lse_s = reinterpret_cast<const float*>(base + 2 * C::TILE_BYTES);
+  // Scores S = Q K^T and dP = dO V^T of the tile in buffer `buf`, both 32-query halves (four
+  // independent MFMA chains).
+  auto scores2 = [&](int buf, f32x16(&sa)[2], f32x16(&dp)[2]) {
+    const char* qtile = smem + buf * BUF;
+    const char* dotile = qtile + C::TILE_BYTES;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      sa[sub] = f32x16{};
+      dp[sub] = f32x16{};
+    }
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        sa[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tile_row16<D>(qtile, 32 * sub + l32, 2 * s + hi), kf[s], sa[sub], 0, 0, 0);
+        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tile_row16<D>(dotile, 32 * sub + l32, 2 * s + hi), vf[s], dp[sub], 0, 0, 0);
+      }
+    }
+  };
+  // P and dS of the tile at query qt in buffer `buf` from its scores, then dV^T += dO^T P and
+  // dK^T += Q^T dS. A half this wave does not see is masked to zero weights.
+  auto grads = [&](int buf, int qt, const f32x16(&sa)[2], const f32x16(&dp)[2]) {
+    const char* qtile = smem + buf * BUF;
+    const char* dotile = qtile + C::TILE_BYTES;
+    const float* lse_s = reinterpret_cast<const float*>(qtile + 2 * C::TILE_BYTES);
     const float* del_s = lse_s + C::TR;
-    const int qt = qt0 + (i - (i / n_qt) * n_qt) * C::TR;
-    {
-      // Both 32-query halves of the tile at once (four independent MFMA chains). A half this
-      // wave does not see costs its MFMAs and is masked to zero weights, which keeps one code
-      // path; a tile neither half of which is seen is skipped.
-      if ((int)block_any<MODE>(qt, kw0, T, window) | (int)block_any<MODE>(qt + 32, kw0, T, window)) {
-        f32x16 sacc[2], dpacc[2];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          sacc[sub] = f32x16{};
-          dpacc[sub] = f32x16{};
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qs = qt + 32 * sub;
+      // Register r: query qs + acc_row(r); lane: key kw0 + l32.
+      const bool all = block_all<MODE>(qs, kw0, T, window);
+      float p[16], ds[16];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 32 * sub + 8 * gq + 4 * hi);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + 32 * sub + 8 * gq + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * gq + e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(sa[sub][r], scale_log2, -l4[e]));
+          if (!all) pr = visible_qk<MODE>(qs + acc_row(r, hi), key, T, window) ? pr : 0.f;
+          p[r] = pr;
+          ds[r] = pr * (dp[sub][r] - d4[e]);
         }
+      }
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 pw, dw;
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                tile_row16<D>(qtile, 32 * sub + l32, 2 * s + hi), kf[s], sacc[sub], 0, 0, 0);
-            dpacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                tile_row16<D>(dotile, 32 * sub + l32, 2 * s + hi), vf[s], dpacc[sub], 0, 0, 0);
-          }
+        for (int e = 0; e < 4; ++e) {
+          pw[e] = pack_bf16x2(p[8 * tt + 2 * e], p[8 * tt + 2 * e + 1]);
+          dw[e] = pack_bf16x2(ds[8 * tt + 2 * e], ds[8 * tt + 2 * e + 1]);
         }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, dw);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const int qs = qt + 32 * sub;
-          // Register r: query qs + acc_row(r); lane: key kw0 + l32.
-          const bool all = block_all<MODE>(qs, kw0, T, window);
-          float p[16], ds[16];
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 32 * sub + 8 * gq + 4 * hi);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + 32 * sub + 8 * gq + 4 * hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * gq + e;
-              float pr = __builtin_amdgcn_exp2f(fmaf(sacc[sub][r], scale_log2, -l4[e]));
-              if (!all) pr = visible_qk<MODE>(qs + acc_row(r, hi), key, T, window) ? pr : 0.f;
-              p[r] = pr;
-              ds[r] = pr * (dpacc[sub][r] - d4[e]);
-            }
-          }
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            u32x4 pw, dw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pw[e] = pack_bf16x2(p[8 * tt + 2 * e], p[8 * tt + 2 * e + 1]);
-              dw[e] = pack_bf16x2(ds[8 * tt + 2 * e], ds[8 * tt + 2 * e + 1]);
-            }
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-            const bf16x8 dsb = __builtin_bit_cast(bf16x8, dw);
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  tile_tr16<D>(dotile, 32 * sub + 16 * tt, db, lane), pb, dva[db], 0, 0, 0);
-              dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  tile_tr16<D>(qtile, 32 * sub + 16 * tt, db, lane), dsb, dka[db], 0, 0, 0);
-            }
-          }
+        for (int db = 0; db < C::DB; ++db) {
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tile_tr16<D>(dotile, 32 * sub + 16 * tt, db, lane), pb, dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tile_tr16<D>(qtile, 32 * sub + 16 * tt, db, lane), dsb, dka[db], 0, 0, 0);
         }
       }
     }
-    if (i + 1 < n_tiles) put((i + 1) & 1);
+  };
+  auto qt_of = [&](int i) { return qt0 + (i - (i / n_qt) * n_qt) * C::TR; };
+  // A tile neither half of which this wave sees is skipped (wave-uniform).
+  auto seen = [&](int i) {
+    const int qt = qt_of(i);
+    return (int)block_any<MODE>(qt, kw0, T, window) | (int)block_any<MODE>(qt + 32, kw0, T, window);
+  };
+
+  if constexpr (PIPE) {
+    // Tile i is used from buffer i % 3 while the scores of tile i + 1 are computed from buffer
+    // (i + 1) % 3 and tile i + 2's loads fly; they are stored into buffer (i + 2) % 3, whose
+    // last readers (tile i - 1) passed the barrier that ended the previous step.
+    fetch(0);
+    put(0);
+    if (n_tiles > 1) {
+      fetch(1);
+      put(1);
+    }
     __syncthreads();
+    f32x16 sa0[2], dp0[2], sa1[2], dp1[2];
+    if (seen(0)) scores2(0, sa0, dp0);
+    int i = 0, buf = 0;
+    auto step = [&](f32x16(&sc)[2], f32x16(&dc)[2], f32x16(&sn)[2], f32x16(&dn)[2]) {
+      const int nb = (buf == 2) ? 0 : buf + 1, nnb = (nb == 2) ? 0 : nb + 1;
+      if (i + 2 < n_tiles) fetch(i + 2);
+      if (i + 1 < n_tiles && seen(i + 1)) scores2(nb, sn, dn);
+      if (seen(i)) grads(buf, qt_of(i), sc, dc);
+      if (i + 2 < n_tiles) put(nnb);
+      __syncthreads();
+      ++i;
+      buf = nb;
+    };
+    while (true) {
+      if (i >= n_tiles) break;
+      step(sa0, dp0, sa1, dp1);
+      if (i >= n_tiles) break;
+      step(sa1, dp1, sa0, dp0);
+    }
+  } else {
+    fetch(0);
+    put(0);
+    __syncthreads();
+    for (int i = 0; i < n_tiles; ++i) {
+      // Tile i + 1's loads fly while tile i is used; they land in the other buffer, whose last
+      // readers (tile i - 1) passed the barrier that ended the previous step.
+      if (i + 1 < n_tiles) fetch(i + 1);
+      if (seen(i)) {
+        f32x16 sa[2], dp[2];
+        scores2(i & 1, sa, dp);
+        grads(i & 1, qt_of(i), sa, dp);
+      }
+      if (i + 1 < n_tiles) put((i + 1) & 1);
+      __syncthreads();
+    }
   }
 
   // Lane l holds key kw0 + l % 32; register r of block db holds d = 32 db + acc_row(r).
