@@ -252,3 +252,28 @@ def test_bwd_validation_with_real_buffers():
     assert call(args(), causal=0, window=3) == _lib.ATTN_ERR_WINDOW
     assert call(args()) == _lib.ATTN_OK
     torch.cuda.synchronize()
+
+
+def test_grouped_order_with_a_partial_group_sampled():
+    """520 heads at T=1024, d=128: the tiles of all heads (0.5 MB each) exceed the cache budget, so
+    the d=128 forward and both backward kernels take the head-grouped order, with a last group of
+    8 heads. Sampled heads from the first group, the partial last group and a random one are
+    checked against the oracle (forward outputs and all three gradients)."""
+    B, H, T, d, window = 65, 8, 1024, 128, 300
+    say(f"grouped order B={B} H={H} T={T} d={d} W={window}")
+    q, k, v, do = (inputs.make_random((B, H, T, d), torch.bfloat16, s) for s in (471, 472, 473, 474))
+    qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
+    out, lse = ops.attn_fwd(qd, kd, vd, window=window)
+    dq, dk, dv = ops.attn_bwd(qd, kd, vd, out, lse, dod, window=window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    heads = [(0, 0), (B - 1, H - 1), (B - 1, 0), (int(rng.integers(B)), int(rng.integers(H)))]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ro, rl = oracle.attention(f64(q[sl]), f64(k[sl]), f64(v[sl]), window=window)
+        eo = float(np.max(np.abs(f64(out[sl]) - ro)))
+        say(f"   head ({b},{h}) forward max|dO|={eo:.3e}")
+        assert eo <= BF16_TOL
+        ref = oracle.attention_backward(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]),
+                                        window=window)
+        check_grads([x[sl].cpu() for x in (dq, dk, dv)], ref, BF16_TOL, f"({b},{h}) ")
