@@ -42,7 +42,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 METRIC = "bf16 causal/SWA attention fwd TFLOP/s + % MFMA peak, T=1024 H=12 d=64"
-ATTN_SOURCE = os.path.join(ROOT, "transformer_attention_qk_amd", "csrc", "attn_fwd_bf16.hip")
+# The attention kernel's source: its own file and the headers it includes, hashed in this order.
+ATTN_SOURCES = [os.path.join(ROOT, "transformer_attention_qk_amd", "csrc", f)
+                for f in ("attn_fwd_bf16.hip", "common.hpp", "launch.hpp", "fastdiv.hpp",
+                          "tile_ops.hpp")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_andrea120m_sssl_traffic.md")
 
 
@@ -72,9 +75,12 @@ def prologue_bytes(B: int, H: int, T: int, d: int, elem: int = 2, tensors: int =
     return B * H * T * 2 * tensors * d * elem
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths: list[str]) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic() -> float | None:
@@ -86,7 +92,7 @@ def measured_traffic() -> float | None:
         return None
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not val or sha.group(1) != source_sha(ATTN_SOURCE):
+    if not sha or not val or sha.group(1) != source_sha(ATTN_SOURCES):
         return None
     return float(val.group(1))
 
