@@ -17,9 +17,13 @@ It prints ONE JSON line on stdout.
 The JSON line also carries "backward": the same layers' gradients (attn_bwd_ex on the normalised
 q, k, then attn_qknorm_rope_bwd_ex), timed with events around each launch; context only.
 
+The line's "cache_states" object times the attention launch alone in two more cache states:
+hot (one layer's launch repeated back to back) and cold (a 512 MiB write before each launch).
+
 --workload autoresearch_default times the train.py listing's default model instead (B=128, H=4,
 T=2048, d=128, eight layers "SSSL" with windows 1024 / 2048) on q, k, v in the projections'
-[B][T][H][d] order, and prints its own JSON line (metric named after that shape).
+[B][T][H][d] order, and prints its own JSON line (metric named after that shape). The other
+bf16 configurations (andrea12m, andrea480m_sssl, long_sssl) run the same way in [B][H][T][d].
 
 Extra modes (used to collect rocprofv3 counters; they print no JSON):
   --only attn|kprologue|attn_unfused|prologue   run only that kernel, --steps times per layer
@@ -42,6 +46,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 METRIC = "bf16 causal/SWA attention fwd TFLOP/s + % MFMA peak, T=1024 H=12 d=64"
+HEADLINE = "andrea120m_sssl"
 # The attention kernel's source: its own file and the headers it includes, hashed in this order.
 ATTN_SOURCES = [os.path.join(ROOT, "transformer_attention_qk_amd", "csrc", f)
                 for f in ("attn_fwd_bf16.hip", "common.hpp", "launch.hpp", "fastdiv.hpp",
@@ -144,7 +149,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 200; 20 for autoresearch_default)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3)")
-    ap.add_argument("--workload", default="andrea120m_sssl")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward and decode timings")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -333,10 +338,33 @@ def main() -> int:
                 t2[l] += b_.elapsed_time(c_) / args.steps
         return t1, t2
 
+    def time_alone(l, before=None) -> float:
+        """Average ms of the attention launch of layer l repeated back to back, events around
+        each launch; before() runs ahead of each launch, outside the events."""
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in ev:
+            if before is not None:
+                before()
+            a_.record()
+            attention(l)
+            b_.record()
+        torch.cuda.synchronize()
+        return sum(a_.elapsed_time(b_) for a_, b_ in ev) / args.steps
+
     # Timed region 1: whole steps, nothing between the kernels (the value).
     ms_per_step = time_steps(step)
     # Timed region 2: the same launches with events around each kernel (the roofline).
     kpro_ms, attn_ms = time_launches(kprologue, attention)
+    # Cache states of the attention launch: "hot" repeats one layer's launch back to back (its
+    # inputs stay in the caches); "cold" writes a 512 MiB buffer (twice the Infinity Cache)
+    # before each launch. The in-model order above (k just written by the prologue) is the
+    # headline state.
+    hot_ms = [time_alone(l) for l in range(L)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold_ms = [time_alone(l, lambda: flush.fill_(1)) for l in range(L)]
+    del flush
     # The two-call path, for comparison.
     ms_per_step_unfused = time_steps(step_unfused)
     pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
@@ -411,14 +439,17 @@ def main() -> int:
     attn_bytes = attn_compulsory_bytes(w.B, w.H, w.T, w.d)
     kpro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=1)
     pro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=2)
-    traffic = measured_traffic() if not model_default else None
+    # the committed counter summary covers the headline workload only
+    traffic = measured_traffic() if w.name == HEADLINE else None
     kernel = (f"attn_fwd_bf16_stream<{w.d}, mode, qkn=true>" if w.d <= 64
               else f"attn_fwd_bf16_tile<{w.d}, mode, qkn=true>")
 
     result = {
-        "metric": METRIC if not model_default else (
+        "metric": METRIC if w.name == HEADLINE else (
             "bf16 causal/SWA attention fwd TFLOP/s + % MFMA peak, train.py default model "
-            "B=128 H=4 T=2048 d=128 [B,T,H,D]"),
+            "B=128 H=4 T=2048 d=128 [B,T,H,D]" if model_default else
+            f"bf16 causal/SWA attention fwd TFLOP/s + % MFMA peak, {w.name} "
+            f"B={w.B} H={w.H} T={w.T} d={w.d}"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -457,6 +488,15 @@ def main() -> int:
             "bytes_per_launch": kpro_bytes,
             "achieved_gbs": round(kpro_bytes * L / (sum(kpro_ms) * 1e-3) / 1e9, 1),
             "peak_gbs": PEAK_HBM_GBS,
+        },
+        "cache_states": {
+            "note": "attention launch alone: hot = one layer's launch repeated back to back; "
+                    "cold = a 512 MiB write before each launch; headline = roofline.launch_us "
+                    "(in-model order, k just written by the prologue)",
+            "hot_launch_us": [round(1e3 * t, 3) for t in hot_ms],
+            "hot_tflops": round(step_flops / (sum(hot_ms) * 1e-3) / 1e12, 3),
+            "cold_launch_us": [round(1e3 * t, 3) for t in cold_ms],
+            "cold_tflops": round(step_flops / (sum(cold_ms) * 1e-3) / 1e12, 3),
         },
         "two_call_path": {
             "ms_per_step": round(ms_per_step_unfused, 5),
