@@ -186,18 +186,18 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const Elem* __restr
 // ---------------------------------------------------------------------------------------------
 // dK, dV (bf16 MFMA).
 // ---------------------------------------------------------------------------------------------
+// Two workgroups per CU (two waves per SIMD) where the registers allow it, d <= 64: a wave's
+// chain of loads, MFMAs and exponentials leaves the SIMD idle between its own instructions, and
+// the second wave fills those gaps. d = 128's accumulators need the whole register file.
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
+__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, Geometry geo, int H_kv, int T, int window_arg,
     float scale_log2, float scale, int nkb, int group_heads) {
   using C = BwdCfg<D>;
-  // Buffers, each: Q tile, dO tile, then LSE (base 2) and D of its 64 queries. d <= 64 runs a
-  // software pipeline over three buffers; d = 128 (whose accumulators leave no registers for a
-  // second set of scores) double-buffers.
-  constexpr bool PIPE = D <= 64;
-  constexpr int NBUF = PIPE ? 3 : 2;
+  // Two buffers, each: Q tile, dO tile, then LSE (base 2) and D of its 64 queries.
+  constexpr int NBUF = 2;
   constexpr int BUF = 2 * C::TILE_BYTES + 2 * C::TR * 4;
   __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF];
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
@@ -351,52 +351,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(
     return (int)block_any<MODE>(qt, kw0, T, window) | (int)block_any<MODE>(qt + 32, kw0, T, window);
   };
 
-  if constexpr (PIPE) {
-    // Tile i is used from buffer i % 3 while the scores of tile i + 1 are computed from buffer
-    // (i + 1) % 3 and tile i + 2's loads fly; they are stored into buffer (i + 2) % 3, whose
-    // last readers (tile i - 1) passed the barrier that ended the previous step.
-    fetch(0);
-    put(0);
-    if (n_tiles > 1) {
-      fetch(1);
-      put(1);
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int i = 0; i < n_tiles; ++i) {
+    // Tile i + 1's loads fly while tile i is used; they land in the other buffer, whose last
+    // readers (tile i - 1) passed the barrier that ended the previous step.
+    if (i + 1 < n_tiles) fetch(i + 1);
+    if (seen(i)) {
+      f32x16 sa[2], dp[2];
+      scores2(i & 1, sa, dp);
+      grads(i & 1, qt_of(i), sa, dp);
     }
+    if (i + 1 < n_tiles) put((i + 1) & 1);
     __syncthreads();
-    f32x16 sa0[2], dp0[2], sa1[2], dp1[2];
-    if (seen(0)) scores2(0, sa0, dp0);
-    int i = 0, buf = 0;
-    auto step = [&](f32x16(&sc)[2], f32x16(&dc)[2], f32x16(&sn)[2], f32x16(&dn)[2]) {
-      const int nb = (buf == 2) ? 0 : buf + 1, nnb = (nb == 2) ? 0 : nb + 1;
-      if (i + 2 < n_tiles) fetch(i + 2);
-      if (i + 1 < n_tiles && seen(i + 1)) scores2(nb, sn, dn);
-      if (seen(i)) grads(buf, qt_of(i), sc, dc);
-      if (i + 2 < n_tiles) put(nnb);
-      __syncthreads();
-      ++i;
-      buf = nb;
-    };
-    while (true) {
-      if (i >= n_tiles) break;
-      step(sa0, dp0, sa1, dp1);
-      if (i >= n_tiles) break;
-      step(sa1, dp1, sa0, dp0);
-    }
-  } else {
-    fetch(0);
-    put(0);
-    __syncthreads();
-    for (int i = 0; i < n_tiles; ++i) {
-      // Tile i + 1's loads fly while tile i is used; they land in the other buffer, whose last
-      // readers (tile i - 1) passed the barrier that ended the previous step.
-      if (i + 1 < n_tiles) fetch(i + 1);
-      if (seen(i)) {
-        f32x16 sa[2], dp[2];
-        scores2(i & 1, sa, dp);
-        grads(i & 1, qt_of(i), sa, dp);
-      }
-      if (i + 1 < n_tiles) put((i + 1) & 1);
-      __syncthreads();
-    }
   }
 
   // Lane l holds key kw0 + l % 32; register r of block db holds d = 32 db + acc_row(r).
