@@ -25,3 +25,10 @@ from .backward import (  # noqa: F401
     rms_norm_backward,
     rope_apply_backward,
 )
+from .value_gate import (  # noqa: F401
+    attention_layer_ve,
+    attention_layer_ve_backward,
+    gate_of,
+    value_gate,
+    value_gate_backward,
+)

@@ -530,6 +530,85 @@ def check_decode(o, seed=15):
         assert np.allclose(out, ro[:, :, n - 1], atol=1e-13) and np.allclose(lse, rl[:, :, n - 1], atol=1e-13)
 
 
+# ---------------------------------------------------------------------------------------------
+# Value-embedding gate (R16): closed forms of the sigmoid, brute force per row, torch's sigmoid,
+# the layer's special cases; its gradients against finite differences and autograd.
+# ---------------------------------------------------------------------------------------------
+
+def check_value_gate(o, seed=16):
+    """gate = 2 sigmoid(z): exactly 1 at z = 0 (the neutral value), 0 and 2 in the limits,
+    gate(z) + gate(-z) = 2; v + gate * ve row by row (pure-Python loop); 2 * torch.sigmoid in
+    float64; a layer whose gates are all 0 equals the layer without the embedding, and one whose
+    gates are all 1 equals the layer on v + ve."""
+    import torch
+
+    rng = _rng(seed)
+    assert o.gate_of(np.array(0.0)) == 1.0
+    assert o.gate_of(np.array(-800.0)) == 0.0 and o.gate_of(np.array(800.0)) == 2.0
+    z = rng.standard_normal(50) * 6
+    assert np.allclose(o.gate_of(z) + o.gate_of(-z), 2.0, rtol=0, atol=1e-15)
+    assert np.allclose(o.gate_of(z), 2 * torch.sigmoid(torch.tensor(z, dtype=torch.float64)).numpy(),
+                       rtol=1e-15, atol=1e-16)
+    assert np.all((o.gate_of(z) > 0) & (o.gate_of(z) < 2))
+    B, H_kv, T, d = 2, 3, 5, 4
+    v = rng.standard_normal((B, H_kv, T, d))
+    ve = rng.standard_normal((B, H_kv, T, d))
+    z = rng.standard_normal((B, H_kv, T)) * 3
+    out = o.value_gate(v, ve, z)
+    for b in range(B):
+        for h in range(H_kv):
+            for t in range(T):
+                gt = 2.0 / (1.0 + math.exp(-z[b, h, t]))
+                for c in range(d):
+                    assert abs(out[b, h, t, c] - (v[b, h, t, c] + gt * ve[b, h, t, c])) < 1e-14
+    H = 6
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, H_kv, T, d))
+    for window in (-1, 2):
+        ro, rl = o.attention_layer(q, k, v, window=window)
+        go, gl = o.attention_layer_ve(q, k, v, ve, np.full(z.shape, -800.0), window=window)
+        assert np.array_equal(ro, go) and np.array_equal(rl, gl)
+        ro, rl = o.attention_layer(q, k, v + ve, window=window)
+        go, gl = o.attention_layer_ve(q, k, v, ve, np.zeros(z.shape), window=window)
+        assert np.array_equal(ro, go) and np.array_equal(rl, gl)
+
+
+def check_value_gate_backward(o, seed=17):
+    """value_gate_backward and attention_layer_ve_backward against central differences of the
+    forward oracle, and against autograd of v + 2 * torch.sigmoid(z) * ve in float64."""
+    import torch
+
+    rng = _rng(seed)
+    B, H_kv, T, d = 1, 2, 4, 3
+    v = rng.standard_normal((B, H_kv, T, d))
+    ve = rng.standard_normal((B, H_kv, T, d))
+    z = rng.standard_normal((B, H_kv, T)) * 2
+    dy = rng.standard_normal((B, H_kv, T, d))
+    loss = lambda: float(np.sum(o.value_gate(v, ve, z) * dy))
+    dv, dve, dz = o.value_gate_backward(ve, z, dy)
+    for x, g in ((v, dv), (ve, dve), (z, dz)):
+        assert np.allclose(g, _fd_grad(loss, x), rtol=0, atol=1e-8)
+    tv, tve, tz = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (v, ve, z))
+    y = tv + 2 * torch.sigmoid(tz)[..., None] * tve
+    gv, gve, gz = torch.autograd.grad((y * torch.tensor(dy)).sum(), (tv, tve, tz))
+    for mine, ref in ((dv, gv), (dve, gve), (dz, gz)):
+        assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-14)
+    H = 4
+    q = rng.standard_normal((B, H, T, d + 1))
+    k = rng.standard_normal((B, H_kv, T, d + 1))
+    v = rng.standard_normal((B, H_kv, T, d + 1))
+    ve = rng.standard_normal((B, H_kv, T, d + 1))
+    do = rng.standard_normal((B, H, T, d + 1))
+    for window in (-1, 1):
+        loss = lambda: float(np.sum(o.attention_layer_ve(q, k, v, ve, z, window=window)[0] * do))
+        grads = o.attention_layer_ve_backward(q, k, v, ve, z, do, window=window)
+        for x, g in zip((q, k, v, ve, z), grads):
+            assert np.allclose(g, _fd_grad(loss, x), rtol=0, atol=3e-7), window
+
+
+VALUE_GATE_CHECKS = [check_value_gate, check_value_gate_backward]
+
+
 BACKWARD_CHECKS = [
     check_backward_finite_differences,
     check_layer_backward_finite_differences,
@@ -555,4 +634,4 @@ ALL_CHECKS = [
     check_sssl_windows,
     check_gqa_head_mapping,
     check_decode,
-] + BACKWARD_CHECKS
+] + BACKWARD_CHECKS + VALUE_GATE_CHECKS

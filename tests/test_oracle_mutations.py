@@ -252,3 +252,55 @@ def test_unmutated_decode_copy_passes():
 ])
 def test_decode_mutations_are_caught(name, kw):
     assert _fails(_mutant(decode_attention=_decode_with(**kw)), [pins.check_decode]), name
+
+
+# Value-embedding gate (R16): each plausible slip in the gate or its gradients fails a pin.
+def _gate_mutant(gate_of=None, value_gate=None, value_gate_backward=None):
+    o = types.SimpleNamespace()
+    for n in ("attention", "attention_layer", "attention_layer_backward", "gate_of", "value_gate",
+              "value_gate_backward", "attention_layer_ve", "attention_layer_ve_backward"):
+        setattr(o, n, getattr(oracle, n))
+    if gate_of is not None:
+        o.gate_of = gate_of
+    if value_gate is not None:
+        o.value_gate = value_gate
+    if value_gate_backward is not None:
+        o.value_gate_backward = value_gate_backward
+    vg = o.value_gate
+    o.attention_layer_ve = lambda q, k, v, ve, z, window=-1, causal=True, eps=1e-6, base=1e4, rows=None: \
+        oracle.attention_layer(q, k, vg(v, ve, z), window, causal, eps, base, rows=rows)
+
+    def layer_bwd(q, k, v, ve, z, dout, window=-1, causal=True, eps=1e-6, base=1e4):
+        dq, dk, dvg = oracle.attention_layer_backward(q, k, vg(v, ve, z), dout, window, causal,
+                                                      eps, base)
+        return (dq, dk) + tuple(o.value_gate_backward(ve, z, dvg))
+    o.attention_layer_ve_backward = layer_bwd
+    return o
+
+
+def _sig(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+
+GATE_MUTANTS = {
+    "gate without the factor 2": dict(gate_of=lambda z: _sig(z)),
+    "gate of -z": dict(gate_of=lambda z: 2 * _sig(-np.asarray(z, np.float64))),
+    "one gate per head, not per token": dict(
+        value_gate=lambda v, ve, z: v + oracle.gate_of(z).mean(axis=-1, keepdims=True)[..., None] * ve),
+    "v and ve swapped": dict(value_gate=lambda v, ve, z: ve + oracle.gate_of(z)[..., None] * v),
+    "dz without the sigmoid's (1 - g/2)": dict(value_gate_backward=lambda ve, z, dy: (
+        dy, oracle.gate_of(z)[..., None] * dy, oracle.gate_of(z) * np.sum(ve * dy, -1))),
+    "dve without the gate": dict(value_gate_backward=lambda ve, z, dy: (
+        dy, dy, oracle.value_gate_backward(ve, z, dy)[2])),
+}
+
+
+def test_unmutated_gate_copy_passes():
+    o = _gate_mutant()
+    for c in pins.VALUE_GATE_CHECKS:
+        c(o)
+
+
+@pytest.mark.parametrize("name", list(GATE_MUTANTS))
+def test_gate_mutations_are_caught(name):
+    assert _fails(_gate_mutant(**GATE_MUTANTS[name]), pins.VALUE_GATE_CHECKS), name
