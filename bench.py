@@ -17,6 +17,9 @@ It prints ONE JSON line on stdout.
 The JSON line also carries "backward": the same layers' gradients (attn_bwd_ex on the normalised
 q, k, then attn_qknorm_rope_bwd_ex), timed with events around each launch; context only.
 
+The "value_gate" object times the same layers with a value embedding (attn_fwd_qknorm_ve_ex:
+the k-only prologue launch also gates v) against the plain layer call, and the gate alone.
+
 The line's "cache_states" object times the attention launch alone in two more cache states:
 hot (one layer's launch repeated back to back) and cold (a 512 MiB write before each launch).
 
@@ -151,7 +154,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward and decode timings")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward, decode and value-gate timings")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue"],
                     default=None)
@@ -369,6 +373,9 @@ def main() -> int:
     ms_per_step_unfused = time_steps(step_unfused)
     pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
 
+    def nothing_step(l):
+        return 0
+
     # Decode (context): one generation step against each layer's keys and values as the cache.
     dec_ms = None
     if not args.no_backward:
@@ -430,6 +437,36 @@ def main() -> int:
             _lib.check("attn_bwd", attention_bwd(l))
             _lib.check("prologue_bwd", prologue_bwd(l))
         bwd_ms, pro_bwd_ms = time_launches(attention_bwd, prologue_bwd)
+
+    # The value-embedding gate (context): each layer as a layer with a value embedding
+    # (attn_fwd_qknorm_ve_ex: the k-only prologue launch also writes the gated v, then the
+    # attention), against the same layer without one, and the gate alone (attn_value_gate_ex).
+    vg_ms = None
+    if not args.no_backward:
+        zshape = (B, T, H) if layout == "bthd" else (B, H, T)
+        ve_l = [inputs.make_random(tuple(v[l].shape), torch.bfloat16, 950 + l).cuda()
+                for l in range(L)]
+        z_l = [inputs.make_random(zshape, torch.bfloat16, 960 + l).cuda() for l in range(L)]
+        vw_l = [torch.empty_like(v[l]) for l in range(L)]
+        PV = [tuple(t.data_ptr() for t in (ve_l[l], z_l[l], vw_l[l])) for l in range(L)]
+
+        def layer_ve(l):
+            pq, pk, pv, _, pkn, po, pl = P[l]
+            pve, pz, pvw = PV[l]
+            return lib.attn_fwd_qknorm_ve_ex(pq, pk, pv, pve, pz, pkn, pvw, po, pl, pcos, psin,
+                                             B, H, H, T, d, lay, eps, windows[l], 1, bf16, stream)
+
+        def gate_alone(l):
+            _, _, pv, _, _, _, _ = P[l]
+            pve, pz, pvw = PV[l]
+            return lib.attn_value_gate_ex(pv, pve, pz, pvw, B, H, T, d, lay, bf16, stream)
+
+        for l in range(L):
+            _lib.check("layer_ve", layer_ve(l))
+            _lib.check("gate_alone", gate_alone(l))
+        lve_ms, lplain_ms = time_launches(layer_ve, layer)
+        vg_ms, _ = time_launches(gate_alone, nothing_step)
+        gate_bytes = B * H * T * (3 * d * 2 + 2)  # v, ve read, v_work written, logits read
 
     flops_layer = [attn_flops(w.B, w.H, w.T, w.d, W) for W in windows]
     step_flops = sum(flops_layer)
@@ -528,6 +565,20 @@ def main() -> int:
             "attn_bwd_tflops": round(2 * step_flops / (sum(bwd_ms) * 1e-3) / 1e12, 3),
             "prologue_bwd_avg_launch_us": round(1e3 * sum(pro_bwd_ms) / L, 3),
             "prologue_bwd_gbs": round(3 * pro_bytes / 2 * L / (sum(pro_bwd_ms) * 1e-3) / 1e9, 1),
+        }
+    if vg_ms is not None:
+        added = (sum(lve_ms) - sum(lplain_ms)) / L
+        result["value_gate"] = {
+            "note": "layers with a value embedding (context): attn_fwd_qknorm_ve_ex, whose k-only "
+                    "prologue launch also gates v, against attn_fwd_qknorm_ex; and the gate alone "
+                    "(attn_value_gate_ex); gate bytes = v, ve read + v_work written + logits",
+            "layer_ve_avg_us": round(1e3 * sum(lve_ms) / L, 3),
+            "layer_avg_us": round(1e3 * sum(lplain_ms) / L, 3),
+            "gate_added_us": round(1e3 * added, 3),
+            "gate_bytes_per_layer": gate_bytes,
+            "gate_added_gbs": round(gate_bytes / (added * 1e-3) / 1e9, 1) if added > 0 else None,
+            "gate_alone_avg_us": round(1e3 * sum(vg_ms) / L, 3),
+            "gate_alone_gbs": round(gate_bytes * L / (sum(vg_ms) * 1e-3) / 1e9, 1),
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, cpu_inputs, windows, args.cpu_budget)

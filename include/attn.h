@@ -217,6 +217,38 @@ int attn_fwd_qknorm_ex(const void* q, const void* k, const void* v, void* k_work
                        int dtype, void* stream);
 
 /*
+ * Value-embedding gate ([HABR] `CausalSelfAttention.forward`, the value-residual step of layers
+ * that have a value embedding): every row of v gets its embedding row added with a gate,
+ *   v'[b][h][t][:] = v[b][h][t][:] + 2 sigmoid(z[b][h][t]) * ve[b][h][t][:]
+ * one gate per (batch, kv head, token), in (0, 2), 1 at z = 0. z is the output of the listing's
+ * `ve_gate` linear layer (a projection, outside this library), the gate logits.
+ *   v, ve        DEVICE, [B][H_kv][T][d] (ATTN_LAYOUT_BHTD) or [B][T][H_kv][d] (ATTN_LAYOUT_BTHD),
+ *                16-byte aligned, dtype elements (read)
+ *   gate_logits  DEVICE, dtype elements, [B][H_kv][T] beside ATTN_LAYOUT_BHTD tensors and
+ *                [B][T][H_kv] beside ATTN_LAYOUT_BTHD ones (read)
+ *   v_out        DEVICE, v's shape (written); may be v itself (in place); any other overlap with
+ *                v, ve or gate_logits is ATTN_ERR_ALIAS
+ *   d in {16, 32, 64, 128}; dtype ATTN_BF16 or ATTN_F32
+ * Arithmetic is fp32 (one rounding of each output for bf16). HBM-bound: reads v, ve and the
+ * logits, writes v_out.
+ */
+int attn_value_gate_ex(const void* v, const void* ve, const void* gate_logits, void* v_out, int B,
+                       int H_kv, int T, int d, int layout, int dtype, void* stream);
+
+/*
+ * attn_fwd_qknorm_ex for a layer with a value embedding: the k-only QK-norm + RoPE kernel also
+ * writes v_work = the gated v (attn_value_gate_ex's rows, in the same launch), then the attention
+ * kernel reads q, k_work and v_work. Arguments as in attn_fwd_qknorm_ex and attn_value_gate_ex;
+ * v_work (written, v's shape) may be v itself. k_work and v_work overlap nothing else that the call
+ * reads or writes, and out and lse overlap none of the inputs (ATTN_ERR_ALIAS). bf16 only.
+ */
+int attn_fwd_qknorm_ve_ex(const void* q, const void* k, const void* v, const void* ve,
+                          const void* gate_logits, void* k_work, void* v_work, void* out,
+                          float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
+                          int H_kv, int T, int d, int layout, float eps, int window, int causal,
+                          int dtype, void* stream);
+
+/*
  * Backward pass of attn_fwd / attn_fwd_ex: the gradients of sum(dout * out) with respect to q, k
  * and v ([HABR] the training step's `loss.backward()` through `CausalSelfAttention.forward`; the
  * gradients are the exact derivatives of the attn_fwd definition). With c = 1/sqrt(d) and
@@ -268,6 +300,19 @@ int attn_qknorm_rope_bwd_ex(const void* q, const void* k, const void* dq_in, con
                             void* dq_out, void* dk_out, const float* cos_tab,
                             const float* sin_tab, int B, int H, int H_kv, int T, int d,
                             int layout, float eps, int dtype, void* stream);
+
+/*
+ * Backward of attn_value_gate_ex: given dv (the gradient of the gated rows v'), with
+ * g = 2 sigmoid(z),
+ *   dve = g * dv,   dgate_logits = g (1 - g / 2) * sum_j ve_j dv_j   (one per row)
+ * and the gradient of v is dv itself (not written). ve, gate_logits, shapes, layout and dtype as
+ * in attn_value_gate_ex; dv is v's shape (read); dve (written, v's shape) may be dv itself;
+ * dgate_logits (written, gate_logits' shape) overlaps nothing else (ATTN_ERR_ALIAS). Arithmetic
+ * is fp32; bf16 outputs are rounded to nearest even.
+ */
+int attn_value_gate_bwd_ex(const void* ve, const void* gate_logits, const void* dv, void* dve,
+                           void* dgate_logits, int B, int H_kv, int T, int d, int layout,
+                           int dtype, void* stream);
 
 /*
  * Decode: one generation step ([GEOM] "A Máscara Causal": inference runs the same masked forward

@@ -31,7 +31,8 @@ def test_header_declares_the_expected_entry_points():
     assert {"attn_fwd", "attn_fwd_qnorm", "attn_fwd_qknorm", "attn_qknorm_rope",
             "attn_rope_table", "attn_strerror", "attn_sssl_windows", "attn_version",
             "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_qknorm_rope_bwd", "attn_decode",
-            "attn_decode_ex", "attn_decode_workspace_bytes"} <= set(names)
+            "attn_decode_ex", "attn_decode_workspace_bytes", "attn_value_gate_ex",
+            "attn_fwd_qknorm_ve_ex", "attn_value_gate_bwd_ex"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -490,6 +491,116 @@ PBWD_CASES = [
 @pytest.mark.parametrize("name,kw,code", PBWD_CASES, ids=[c[0] for c in PBWD_CASES])
 def test_qknorm_rope_bwd_rejects_before_any_hip_call(lib, name, kw, code):
     assert _pbwd(lib, **kw) == code, name
+
+
+# ---------------------------------------------------------------------------------------------
+# Value-embedding gate.
+# ---------------------------------------------------------------------------------------------
+
+_VG = {n: (i + 1) * P for i, n in enumerate(("v", "ve", "z", "vo"))}
+
+
+def _vg(lib, **kw):
+    a = dict(_VG, B=1, H_kv=2, T=64, d=64, layout=0, dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_value_gate_ex(a["v"], a["ve"], a["z"], a["vo"], a["B"], a["H_kv"], a["T"],
+                                  a["d"], a["layout"], a["dtype"], None)
+
+
+VG_CASES = [
+    ("null v", dict(v=None), _lib.ATTN_ERR_NULL),
+    ("null ve", dict(ve=None), _lib.ATTN_ERR_NULL),
+    ("null logits", dict(z=None), _lib.ATTN_ERR_NULL),
+    ("null v_out", dict(vo=None), _lib.ATTN_ERR_NULL),
+    ("dtype 7", dict(dtype=7), _lib.ATTN_ERR_DTYPE),
+    ("d=24", dict(d=24), _lib.ATTN_ERR_HEAD_DIM),
+    ("B=0", dict(B=0), _lib.ATTN_ERR_SHAPE),
+    ("layout 2", dict(layout=2), _lib.ATTN_ERR_ARG),
+    ("misaligned v", dict(v=_VG["v"] + 4), _lib.ATTN_ERR_ALIGN),
+    ("misaligned bf16 logits", dict(z=_VG["z"] + 1), _lib.ATTN_ERR_ALIGN),
+    ("misaligned f32 logits", dict(z=_VG["z"] + 2, dtype=_lib.ATTN_F32), _lib.ATTN_ERR_ALIGN),
+    ("v_out inside v", dict(vo=_VG["v"] + 16), _lib.ATTN_ERR_ALIAS),
+    ("v_out is ve", dict(vo=_VG["ve"]), _lib.ATTN_ERR_ALIAS),
+    ("v_out over the logits", dict(vo=_VG["z"] - 64), _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", VG_CASES, ids=[c[0] for c in VG_CASES])
+def test_value_gate_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _vg(lib, **kw) == code, name
+
+
+_VF = {n: (i + 1) * P for i, n in enumerate(("q", "k", "v", "ve", "z", "kw", "vw", "out", "lse",
+                                             "cos", "sin"))}
+
+
+def _vfused(lib, **kw):
+    a = dict(_VF, B=1, H=4, H_kv=2, T=64, d=64, layout=0, eps=1e-6, window=-1, causal=1,
+             dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_fwd_qknorm_ve_ex(a["q"], a["k"], a["v"], a["ve"], a["z"], a["kw"], a["vw"],
+                                     a["out"], a["lse"], a["cos"], a["sin"], a["B"], a["H"],
+                                     a["H_kv"], a["T"], a["d"], a["layout"], a["eps"],
+                                     a["window"], a["causal"], a["dtype"], None)
+
+
+VF_CASES = [
+    ("null ve", dict(ve=None), _lib.ATTN_ERR_NULL),
+    ("null logits", dict(z=None), _lib.ATTN_ERR_NULL),
+    ("null v_work", dict(vw=None), _lib.ATTN_ERR_NULL),
+    ("null k", dict(k=None), _lib.ATTN_ERR_NULL),
+    ("f32", dict(dtype=_lib.ATTN_F32), _lib.ATTN_ERR_DTYPE),
+    ("d=16", dict(d=16), _lib.ATTN_ERR_HEAD_DIM),
+    ("window -2", dict(window=-2), _lib.ATTN_ERR_WINDOW),
+    ("H_kv does not divide H", dict(H_kv=3), _lib.ATTN_ERR_SHAPE),
+    ("misaligned ve", dict(ve=_VF["ve"] + 8), _lib.ATTN_ERR_ALIGN),
+    ("v_work inside v", dict(vw=_VF["v"] + 16), _lib.ATTN_ERR_ALIAS),
+    ("v_work is k_work", dict(vw=_VF["kw"]), _lib.ATTN_ERR_ALIAS),
+    ("v_work is ve", dict(vw=_VF["ve"]), _lib.ATTN_ERR_ALIAS),
+    ("k_work is v", dict(kw=_VF["v"]), _lib.ATTN_ERR_ALIAS),
+    ("k_work over the logits", dict(kw=_VF["z"]), _lib.ATTN_ERR_ALIAS),
+    ("out is ve", dict(out=_VF["ve"]), _lib.ATTN_ERR_ALIAS),
+    ("out is v", dict(out=_VF["v"]), _lib.ATTN_ERR_ALIAS),
+    ("lse over the logits", dict(lse=_VF["z"]), _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", VF_CASES, ids=[c[0] for c in VF_CASES])
+def test_attn_fwd_qknorm_ve_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _vfused(lib, **kw) == code, name
+
+
+_VB = {n: (i + 1) * P for i, n in enumerate(("ve", "z", "dv", "dve", "dz"))}
+
+
+def _vgb(lib, **kw):
+    a = dict(_VB, B=2, H_kv=2, T=64, d=32, layout=1, dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_value_gate_bwd_ex(a["ve"], a["z"], a["dv"], a["dve"], a["dz"], a["B"],
+                                      a["H_kv"], a["T"], a["d"], a["layout"], a["dtype"], None)
+
+
+VGB_CASES = [
+    ("null dv", dict(dv=None), _lib.ATTN_ERR_NULL),
+    ("null dve", dict(dve=None), _lib.ATTN_ERR_NULL),
+    ("null dlogits", dict(dz=None), _lib.ATTN_ERR_NULL),
+    ("dtype 2", dict(dtype=2), _lib.ATTN_ERR_DTYPE),
+    ("d=48", dict(d=48), _lib.ATTN_ERR_HEAD_DIM),
+    ("misaligned dlogits", dict(dz=_VB["dz"] + 1), _lib.ATTN_ERR_ALIGN),
+    ("dve inside dv", dict(dve=_VB["dv"] + 16), _lib.ATTN_ERR_ALIAS),
+    ("dve is ve", dict(dve=_VB["ve"]), _lib.ATTN_ERR_ALIAS),
+    ("dlogits are the logits", dict(dz=_VB["z"]), _lib.ATTN_ERR_ALIAS),
+    ("dlogits inside dve", dict(dz=_VB["dve"] + 64), _lib.ATTN_ERR_ALIAS),
+    ("dlogits inside dv", dict(dz=_VB["dv"] + 64), _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", VGB_CASES, ids=[c[0] for c in VGB_CASES])
+def test_value_gate_bwd_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _vgb(lib, **kw) == code, name
 
 
 # ---------------------------------------------------------------------------------------------

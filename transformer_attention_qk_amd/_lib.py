@@ -48,6 +48,10 @@ SIGNATURES = {
     "attn_bwd_ex": (c_int, [c_void_p] * 10 + [c_int] * 9 + [c_void_p]),
     "attn_qknorm_rope_bwd": (c_int, [c_void_p] * 8 + [c_int] * 4 + [c_float, c_int, c_void_p]),
     "attn_qknorm_rope_bwd_ex": (c_int, [c_void_p] * 8 + [c_int] * 6 + [c_float, c_int, c_void_p]),
+    "attn_value_gate_ex": (c_int, [c_void_p] * 4 + [c_int] * 6 + [c_void_p]),
+    "attn_fwd_qknorm_ve_ex": (c_int, [c_void_p] * 11 + [c_int] * 6 + [c_float] + [c_int] * 3
+                              + [c_void_p]),
+    "attn_value_gate_bwd_ex": (c_int, [c_void_p] * 5 + [c_int] * 6 + [c_void_p]),
     "attn_decode_workspace_bytes": (ctypes.c_longlong, [c_int] * 5),
     "attn_decode": (c_int, [c_void_p] * 7 + [ctypes.c_longlong] + [c_int] * 6 + [c_void_p]),
     "attn_decode_ex": (c_int, [c_void_p] * 7 + [ctypes.c_longlong] + [c_int] * 8 + [c_void_p]),

@@ -282,6 +282,123 @@ int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, v
 }
 
 // ---------------------------------------------------------------------------------------------
+// Value-embedding gate.
+// ---------------------------------------------------------------------------------------------
+
+namespace {
+
+// Shape, dtype and alignment checks of a gate call on [B][H_kv][T][d] rows (layout as given);
+// gb = bytes of the gate logits (one element per row).
+int check_gate_dims(const void* v, const void* ve, const void* z, int B, int H_kv, int T, int d,
+                    int layout, int dtype, attn::Dims* dm, int64_t* vb, int64_t* gb) {
+  if (!v || !ve || !z) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_dims(B, H_kv, H_kv, T, d, layout, dm, &n_q, &n_kv)) return rc;
+  if (!aligned16(v) || !aligned16(ve) ||
+      (reinterpret_cast<uintptr_t>(z) & (uintptr_t)(elem_bytes(dtype) - 1)))
+    return ATTN_ERR_ALIGN;
+  *vb = n_kv * elem_bytes(dtype);
+  *gb = (int64_t)B * H_kv * T * elem_bytes(dtype);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+int attn_value_gate_ex(const void* v, const void* ve, const void* gate_logits, void* v_out, int B,
+                       int H_kv, int T, int d, int layout, int dtype, void* stream) {
+  if (!v_out) return ATTN_ERR_NULL;
+  attn::Dims dm;
+  int64_t vb = 0, gb = 0;
+  if (int rc = check_gate_dims(v, ve, gate_logits, B, H_kv, T, d, layout, dtype, &dm, &vb, &gb))
+    return rc;
+  if (!aligned16(v_out)) return ATTN_ERR_ALIGN;
+  if (v_out != v && overlap(v_out, vb, v, vb)) return ATTN_ERR_ALIAS;
+  if (overlap(v_out, vb, ve, vb) || overlap(v_out, vb, gate_logits, gb)) return ATTN_ERR_ALIAS;
+  attn::GateArgs vg;
+  vg.v = v;
+  vg.ve = ve;
+  vg.z = gate_logits;
+  vg.v_out = v_out;
+  const hipError_t e = attn::launch_qknorm_rope(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                nullptr, dm, 0.0f, dtype, (hipStream_t)stream, vg);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_qknorm_ve_ex(const void* q, const void* k, const void* v, const void* ve,
+                          const void* gate_logits, void* k_work, void* v_work, void* out,
+                          float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
+                          int H_kv, int T, int d, int layout, float eps, int window, int causal,
+                          int dtype, void* stream) {
+  if (!k_work || !v_work) return ATTN_ERR_NULL;
+  attn::Dims dm;
+  int64_t n_q = 0, n_kv = 0;
+  if (int rc = check_qnorm_args(q, k_work, v_work, out, lse, cos_tab, sin_tab, B, H, H_kv, T, d,
+                                layout, eps, window, causal, dtype, &dm, &n_q, &n_kv))
+    return rc;
+  attn::Dims dg;
+  int64_t vb = 0, gb = 0;
+  if (int rc = check_gate_dims(v, ve, gate_logits, B, H_kv, T, d, layout, dtype, &dg, &vb, &gb))
+    return rc;
+  if (!k) return ATTN_ERR_NULL;
+  if (!aligned16(k)) return ATTN_ERR_ALIGN;
+  if (2 * (int64_t)B * H + 2 > 0x7fffffff) return ATTN_ERR_SHAPE;  // rows of k and v, as int
+  const int64_t qb = n_q * 2, kb = n_kv * 2;
+  // k_work may be k and v_work may be v (in place); nothing else written overlaps anything read.
+  if (k_work != k && overlap(k_work, kb, k, kb)) return ATTN_ERR_ALIAS;
+  if (v_work != v && overlap(v_work, kb, v, kb)) return ATTN_ERR_ALIAS;
+  if (overlap(k_work, kb, q, qb) || overlap(k_work, kb, v, kb) || overlap(k_work, kb, ve, kb) ||
+      overlap(k_work, kb, gate_logits, gb) || overlap(k_work, kb, v_work, kb))
+    return ATTN_ERR_ALIAS;
+  if (overlap(v_work, kb, q, qb) || overlap(v_work, kb, k, kb) || overlap(v_work, kb, ve, kb) ||
+      overlap(v_work, kb, gate_logits, gb))
+    return ATTN_ERR_ALIAS;
+  if (overlap(out, qb, k, kb) || overlap(out, qb, v, kb) || overlap(out, qb, ve, kb) ||
+      overlap(out, qb, gate_logits, gb))
+    return ATTN_ERR_ALIAS;
+  if (lse != nullptr) {
+    const int64_t lbytes = (int64_t)B * H * T * 4;
+    if (overlap(lse, lbytes, k, kb) || overlap(lse, lbytes, v, kb) ||
+        overlap(lse, lbytes, ve, kb) || overlap(lse, lbytes, gate_logits, gb))
+      return ATTN_ERR_ALIAS;
+  }
+  attn::GateArgs vg;
+  vg.v = v;
+  vg.ve = ve;
+  vg.z = gate_logits;
+  vg.v_out = v_work;
+  hipError_t e = attn::launch_qknorm_rope(nullptr, k, nullptr, k_work, cos_tab, sin_tab, dm, eps,
+                                          ATTN_BF16, (hipStream_t)stream, vg);
+  if (e == hipSuccess)
+    e = attn::launch_attn_fwd_bf16_qknorm(q, k_work, v_work, out, lse, cos_tab, sin_tab, eps, dm,
+                                          window, causal, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_value_gate_bwd_ex(const void* ve, const void* gate_logits, const void* dv, void* dve,
+                           void* dgate_logits, int B, int H_kv, int T, int d, int layout,
+                           int dtype, void* stream) {
+  if (!dve || !dgate_logits) return ATTN_ERR_NULL;
+  attn::Dims dm;
+  int64_t vb = 0, gb = 0;
+  // dv takes v's place in the shape checks
+  if (int rc = check_gate_dims(dv, ve, gate_logits, B, H_kv, T, d, layout, dtype, &dm, &vb, &gb))
+    return rc;
+  if (!aligned16(dve) ||
+      (reinterpret_cast<uintptr_t>(dgate_logits) & (uintptr_t)(elem_bytes(dtype) - 1)))
+    return ATTN_ERR_ALIGN;
+  if (dve != dv && overlap(dve, vb, dv, vb)) return ATTN_ERR_ALIAS;
+  if (overlap(dve, vb, ve, vb) || overlap(dve, vb, gate_logits, gb) ||
+      overlap(dgate_logits, gb, ve, vb) || overlap(dgate_logits, gb, gate_logits, gb) ||
+      overlap(dgate_logits, gb, dv, vb) || overlap(dgate_logits, gb, dve, vb))
+    return ATTN_ERR_ALIAS;
+  const hipError_t e = attn::launch_value_gate_bwd(ve, gate_logits, dv, dve, dgate_logits, dm,
+                                                   dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Backward pass.
 // ---------------------------------------------------------------------------------------------
 

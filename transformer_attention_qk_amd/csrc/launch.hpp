@@ -61,10 +61,22 @@ inline int group_heads(int n_heads, int64_t bytes_per_head) {
 hipError_t launch_rope_table(float* cos_tab, float* sin_tab, int T, int d, double base,
                              hipStream_t stream);
 
-// dtype: 0 = bf16, 1 = f32. d in {16, 32, 64, 128}. q == nullptr: k rows only (q_out unused).
+// Value-embedding gate rows of a prologue launch: v_out = v + 2 sigmoid(z) ve (v == nullptr: none).
+struct GateArgs {
+  const void *v = nullptr, *ve = nullptr, *z = nullptr;
+  void* v_out = nullptr;
+};
+
+// dtype: 0 = bf16, 1 = f32. d in {16, 32, 64, 128}. q == nullptr: no q rows (q_out unused);
+// k == nullptr: no k rows (then vg must name v rows).
 hipError_t launch_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
                               const float* cos_tab, const float* sin_tab, const Dims& dm,
-                              float eps, int dtype, hipStream_t stream);
+                              float eps, int dtype, hipStream_t stream,
+                              const GateArgs& vg = GateArgs{});
+
+// Backward of the gate: dve = g dv, dz = g (1 - g/2) sum_j ve_j dv_j with g = 2 sigmoid(z).
+hipError_t launch_value_gate_bwd(const void* ve, const void* z, const void* dv, void* dve,
+                                 void* dz, const Dims& dm, int dtype, hipStream_t stream);
 
 // bf16 attention on MFMA. d in {32, 64, 128}.
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -84,11 +84,18 @@ constexpr int kE = (sizeof(Elem) == 2) ? 8 : 4;
 // element j < d/2 and its rotation partner j + d/2 sit in lanes i and i ^ (L/2), which swap
 // their chunks with one xor shuffle per 32-bit word; the sum of squares crosses the L lanes by
 // xor shuffles too. A row group loads the rotation factors of its position once for its R rows.
-template <typename Elem, int D, int R>
+//
+// VG: the launch also applies the value-embedding gate ("Подробный технический разбор реализации
+// Autoresearch", train.py listing, `CausalSelfAttention.forward`: v + 2 sigmoid(gate logit) ve,
+// one gate per token and kv head) to the B*H_kv rows of v, which follow the other rows from head
+// index v_start (a multiple of R, so no block mixes the two kinds of row). v, ve and v_out share
+// k's strides; the gate logits z sit at b * sz.b + h * sz.h + t * sz.t.
+template <typename Elem, int D, int R, bool VG>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const Elem* __restrict__ q, const Elem* __restrict__ k, Elem* q_out, Elem* k_out,
     const float* __restrict__ cos_tab, const float* __restrict__ sin_tab, Strides sq, Strides sk,
-    FastDiv H, FastDiv H_kv, int heads_q, int heads, int T, FastDiv t_blocks, float eps) {
+    FastDiv H, FastDiv H_kv, int heads_q, int heads, int T, FastDiv t_blocks, float eps,
+    const Elem* v, const Elem* ve, const Elem* zg, Elem* v_out, Strides sz, int v_start) {
   constexpr int E = kE<Elem>;
   constexpr int HALF = D / 2;
   constexpr int L = D / E;      // lanes per row (2 .. 32)
@@ -107,6 +114,28 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   const bool first = sub < L / 2;
   const int j0 = (sub % (L / 2)) * E;  // frequency of the chunk's first element
   const int total = heads_q + heads;
+  if constexpr (VG) {
+    if (h0 >= v_start) {  // block-uniform: rows of v
+      const int lane_v = r_loc * sk.t + sub * E;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int hv = h0 + r - v_start;
+        if (hv >= heads) break;
+        const uint32_t b = H_kv.div((uint32_t)hv), hk = (uint32_t)hv - b * H_kv.d;
+        const int64_t base = (int64_t)b * sk.b + (int64_t)hk * sk.h + (int64_t)t0 * sk.t;
+        const float z = (float)zg[(int64_t)b * sz.b + (int64_t)hk * sz.h + (int64_t)t * sz.t];
+        float x[E], e[E], y[E];
+        Vec<Elem, E>::load(v + base + lane_v, x);
+        Vec<Elem, E>::load(ve + base + lane_v, e);
+        // 2 sigmoid(z) in (0, 2): 0 for z -> -inf (exp overflows to inf), 2 for z -> +inf
+        const float g = 2.0f / (1.0f + expf(-z));
+#pragma unroll
+        for (int i = 0; i < E; ++i) y[i] = fmaf(g, e[i], x[i]);
+        if (valid) Vec<Elem, E>::store(v_out + base + lane_v, y);
+      }
+      return;
+    }
+  }
 
   // A row's element offset splits into a block-uniform part (head h at position t0) and this
   // lane's part, which stays below 2^31 (TPB row strides; the host bounds H * d).
@@ -292,10 +321,89 @@ hipError_t launch_qknorm_rope_bwd(const void* q, const void* k, const void* dq_i
   return hipErrorInvalidValue;
 }
 
+// Backward of the value-embedding gate for the B*H_kv rows of v: with g = 2 sigmoid(z) and dv the
+// gradient of the gated rows, dve = g dv and dz = g (1 - g/2) sum_j ve_j dv_j (the derivative of
+// 2 sigmoid is 2 sigmoid (1 - sigmoid)); the gradient of v itself is dv unchanged. Same row
+// grouping as the prologue: L lanes per row, the row sum crossing them by xor shuffles; lane 0 of
+// a row writes dz. dve may be dv itself (each lane reads its chunk before writing it).
 template <typename Elem, int D>
+__global__ __launch_bounds__(256) void value_gate_bwd_kernel(
+    const Elem* __restrict__ ve, const Elem* __restrict__ zg, const Elem* dv, Elem* dve,
+    Elem* __restrict__ dz, Strides sk, Strides sz, FastDiv H_kv, int T, FastDiv t_blocks) {
+  constexpr int E = kE<Elem>;
+  constexpr int L = D / E;
+  constexpr int TPB = 256 / L;
+  const int h = (int)t_blocks.div(blockIdx.x);  // block-uniform: kv head row b * H_kv + hk
+  const int tb = (int)blockIdx.x - h * (int)t_blocks.d;
+  const int t_loc = (int)threadIdx.x / L;
+  const int t0 = tb * TPB;
+  const bool valid = t0 + t_loc < T;
+  const int t = valid ? t0 + t_loc : T - 1;
+  const int sub = (int)threadIdx.x % L;
+  const uint32_t b = H_kv.div((uint32_t)h), hk = (uint32_t)h - b * H_kv.d;
+  const int64_t off = (int64_t)b * sk.b + (int64_t)hk * sk.h + (int64_t)t * sk.t + sub * E;
+  const int64_t zoff = (int64_t)b * sz.b + (int64_t)hk * sz.h + (int64_t)t * sz.t;
+  const float z = (float)zg[zoff];
+  float e[E], g_in[E], out[E];
+  Vec<Elem, E>::load(ve + off, e);
+  Vec<Elem, E>::load(dv + off, g_in);
+  const float g = 2.0f / (1.0f + expf(-z));
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    dot = fmaf(e[i], g_in[i], dot);
+    out[i] = g * g_in[i];
+  }
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+  if (valid) {
+    Vec<Elem, E>::store(dve + off, out);
+    if (sub == 0) dz[zoff] = (Elem)(g * (1.0f - 0.5f * g) * dot);
+  }
+}
+
+template <typename Elem, int D>
+static hipError_t launch_value_gate_bwd_t(const void* ve, const void* z, const void* dv, void* dve,
+                                          void* dz, const Dims& dm, hipStream_t stream) {
+  constexpr int L = D / kE<Elem>;
+  constexpr int TPB = 256 / L;
+  const int T = dm.T;
+  const Geometry geo = make_geometry(dm);
+  const int t_blocks = (T + TPB - 1) / TPB;
+  const int64_t grid = (int64_t)t_blocks * dm.B * dm.H_kv;
+  const Strides sz = (dm.layout == 0) ? Strides{(int64_t)dm.H_kv * T, T, 1}
+                                      : Strides{(int64_t)T * dm.H_kv, 1, dm.H_kv};
+  hipLaunchKernelGGL((value_gate_bwd_kernel<Elem, D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const Elem*)ve, (const Elem*)z, (const Elem*)dv, (Elem*)dve, (Elem*)dz,
+                     geo.kv, sz, make_fastdiv((uint32_t)dm.H_kv), T,
+                     make_fastdiv((uint32_t)t_blocks));
+  return hipGetLastError();
+}
+
+hipError_t launch_value_gate_bwd(const void* ve, const void* z, const void* dv, void* dve,
+                                 void* dz, const Dims& dm, int dtype, hipStream_t stream) {
+  const int d = dm.d;
+#define ATTN_VGB_CASE(ELEM, DD) \
+  if (d == DD) return launch_value_gate_bwd_t<ELEM, DD>(ve, z, dv, dve, dz, dm, stream);
+  if (dtype == 0) {
+    ATTN_VGB_CASE(bf16, 16)
+    ATTN_VGB_CASE(bf16, 32)
+    ATTN_VGB_CASE(bf16, 64)
+    ATTN_VGB_CASE(bf16, 128)
+  } else {
+    ATTN_VGB_CASE(float, 16)
+    ATTN_VGB_CASE(float, 32)
+    ATTN_VGB_CASE(float, 64)
+    ATTN_VGB_CASE(float, 128)
+  }
+#undef ATTN_VGB_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename Elem, int D, bool VG>
 static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out, void* k_out,
                                        const float* cos_tab, const float* sin_tab, const Dims& dm,
-                                       float eps, hipStream_t stream) {
+                                       float eps, const GateArgs& vg, hipStream_t stream) {
   constexpr int R = 2;  // rows per lane
   constexpr int L = D / kE<Elem>;
   constexpr int TPB = 256 / L;
@@ -303,21 +411,36 @@ static hipError_t launch_qknorm_rope_t(const void* q, const void* k, void* q_out
   const Geometry geo = make_geometry(dm);
   const int heads = dm.B * dm.H_kv;
   const int heads_q = (q != nullptr) ? dm.B * dm.H : 0;
+  // Rows: q's (if any), k's (if any), then, with the gate, v's from a multiple of R.
+  if (k == nullptr && (q != nullptr || !VG)) return hipErrorInvalidValue;
+  const int qk_rows = heads_q + ((k != nullptr) ? heads : 0);
+  const int v_start = VG ? (qk_rows + R - 1) / R * R : qk_rows;
+  const int rows = VG ? v_start + heads : qk_rows;
   const int t_blocks = (T + TPB - 1) / TPB;
-  const int64_t grid = (int64_t)t_blocks * ((heads_q + heads + R - 1) / R);
-  hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D, R>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, cos_tab, sin_tab,
-                     geo.q, geo.kv, make_fastdiv((uint32_t)dm.H), make_fastdiv((uint32_t)dm.H_kv),
-                     heads_q, heads, T, make_fastdiv((uint32_t)t_blocks), eps);
+  const int64_t grid = (int64_t)t_blocks * ((rows + R - 1) / R);
+  // gate logits: [B][H_kv][T] beside [B][H_kv][T][d] tensors, [B][T][H_kv] beside [B][T][H_kv][d]
+  const Strides sz = (dm.layout == 0) ? Strides{(int64_t)dm.H_kv * T, T, 1}
+                                      : Strides{(int64_t)T * dm.H_kv, 1, dm.H_kv};
+  hipLaunchKernelGGL((qknorm_rope_kernel<Elem, D, R, VG>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, (const Elem*)q, (const Elem*)k, (Elem*)q_out, (Elem*)k_out, cos_tab,
+                     sin_tab, geo.q, geo.kv, make_fastdiv((uint32_t)dm.H),
+                     make_fastdiv((uint32_t)dm.H_kv), heads_q, heads, T,
+                     make_fastdiv((uint32_t)t_blocks), eps, (const Elem*)vg.v, (const Elem*)vg.ve,
+                     (const Elem*)vg.z, (Elem*)vg.v_out, sz, v_start);
   return hipGetLastError();
 }
 
 hipError_t launch_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
                               const float* cos_tab, const float* sin_tab, const Dims& dm,
-                              float eps, int dtype, hipStream_t stream) {
+                              float eps, int dtype, hipStream_t stream, const GateArgs& vg) {
   const int d = dm.d;
-#define ATTN_QKN_CASE(ELEM, DD) \
-  if (d == DD) return launch_qknorm_rope_t<ELEM, DD>(q, k, q_out, k_out, cos_tab, sin_tab, dm, eps, stream);
+  const bool gate = vg.v != nullptr;
+#define ATTN_QKN_CASE(ELEM, DD)                                                                 \
+  if (d == DD)                                                                                  \
+    return gate ? launch_qknorm_rope_t<ELEM, DD, true>(q, k, q_out, k_out, cos_tab, sin_tab, dm, \
+                                                       eps, vg, stream)                          \
+                : launch_qknorm_rope_t<ELEM, DD, false>(q, k, q_out, k_out, cos_tab, sin_tab,    \
+                                                        dm, eps, vg, stream);
   if (dtype == 0) {
     ATTN_QKN_CASE(bf16, 16)
     ATTN_QKN_CASE(bf16, 32)

@@ -289,6 +289,104 @@ def attention_layer_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return dq, dk, dv
 
 
+def _gate_shape(v: torch.Tensor, layout: str) -> tuple[int, int, int, int, tuple]:
+    """(B, H_kv, T, d, logits shape) of v stored in `layout`."""
+    if v.dim() != 4:
+        raise ValueError("v must be 4-D")
+    if layout == "bhtd":
+        B, H_kv, T, d = v.shape
+        return B, H_kv, T, d, (B, H_kv, T)
+    B, T, H_kv, d = v.shape
+    return B, H_kv, T, d, (B, T, H_kv)
+
+
+def value_gate(v: torch.Tensor, ve: torch.Tensor, gate_logits: torch.Tensor,
+               out: torch.Tensor | None = None, layout: str = "bhtd") -> torch.Tensor:
+    """v + 2 sigmoid(gate_logits) ve per row (attn_value_gate_ex); out may be v (in place)."""
+    lib = _lib.load()
+    _require(v, "v")
+    if v.dtype not in _DTYPES:
+        raise ValueError("v must be bf16 or fp32")
+    B, H_kv, T, d, zs = _gate_shape(v, layout)
+    _require(ve, "ve", v.shape, v.dtype)
+    _require(gate_logits, "gate_logits", zs, v.dtype)
+    out = torch.empty_like(v) if out is None else out
+    _require(out, "out", v.shape, v.dtype)
+    rc = lib.attn_value_gate_ex(_ptr(v), _ptr(ve), _ptr(gate_logits), _ptr(out), B, H_kv, T, d,
+                                _LAYOUTS[layout], _DTYPES[v.dtype], _stream_handle())
+    _lib.check("attn_value_gate_ex", rc)
+    return out
+
+
+def value_gate_bwd(ve: torch.Tensor, gate_logits: torch.Tensor, dv: torch.Tensor,
+                   dve: torch.Tensor | None = None, dgate_logits: torch.Tensor | None = None,
+                   layout: str = "bhtd"):
+    """(dve, dgate_logits) of the gate given dv, the gradient of the gated rows
+    (attn_value_gate_bwd_ex); the gradient of v is dv itself. dve may be dv (in place)."""
+    lib = _lib.load()
+    _require(dv, "dv")
+    if dv.dtype not in _DTYPES:
+        raise ValueError("dv must be bf16 or fp32")
+    B, H_kv, T, d, zs = _gate_shape(dv, layout)
+    _require(ve, "ve", dv.shape, dv.dtype)
+    _require(gate_logits, "gate_logits", zs, dv.dtype)
+    dve = torch.empty_like(dv) if dve is None else dve
+    _require(dve, "dve", dv.shape, dv.dtype)
+    dgate_logits = torch.empty_like(gate_logits) if dgate_logits is None else dgate_logits
+    _require(dgate_logits, "dgate_logits", zs, dv.dtype)
+    rc = lib.attn_value_gate_bwd_ex(_ptr(ve), _ptr(gate_logits), _ptr(dv), _ptr(dve),
+                                    _ptr(dgate_logits), B, H_kv, T, d, _LAYOUTS[layout],
+                                    _DTYPES[dv.dtype], _stream_handle())
+    _lib.check("attn_value_gate_bwd_ex", rc)
+    return dve, dgate_logits
+
+
+def attn_fwd_qknorm_ve(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ve: torch.Tensor,
+                       gate_logits: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                       window: int = -1, causal: bool = True, eps: float = 1e-6,
+                       k_work: torch.Tensor | None = None, v_work: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       want_lse: bool = True, layout: str = "bhtd"):
+    """A layer with a value embedding in one library call (attn_fwd_qknorm_ve_ex): QK-norm +
+    RoPE of raw bf16 q, k, the gate on v, then attention. Returns (out, lse, k_work, v_work)."""
+    lib = _lib.load()
+    _require(q, "q", dtype=torch.bfloat16)
+    _require(k, "k", dtype=q.dtype)
+    B, H, H_kv, T, d = _geometry(q, k, layout)
+    _require(v, "v", k.shape, q.dtype)
+    _require(ve, "ve", k.shape, q.dtype)
+    _require(gate_logits, "gate_logits", _gate_shape(v, layout)[4], q.dtype)
+    _rope_tables(cos, sin, T, d)
+    k_work = torch.empty_like(k) if k_work is None else k_work
+    _require(k_work, "k_work", k.shape, q.dtype)
+    v_work = torch.empty_like(v) if v_work is None else v_work
+    _require(v_work, "v_work", v.shape, q.dtype)
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.shape, q.dtype)
+    lse = _lse(lse, want_lse, B, H, T, q.device)
+    rc = lib.attn_fwd_qknorm_ve_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(gate_logits),
+                                   _ptr(k_work), _ptr(v_work), _ptr(out), _ptr(lse), _ptr(cos),
+                                   _ptr(sin), B, H, H_kv, T, d, _LAYOUTS[layout], float(eps),
+                                   int(window), int(bool(causal)), _lib.ATTN_BF16,
+                                   _stream_handle())
+    _lib.check("attn_fwd_qknorm_ve_ex", rc)
+    return out, lse, k_work, v_work
+
+
+def attention_layer_ve_backward(q: torch.Tensor, k: torch.Tensor, v_work: torch.Tensor,
+                                ve: torch.Tensor, gate_logits: torch.Tensor, out: torch.Tensor,
+                                lse: torch.Tensor, dout: torch.Tensor, cos: torch.Tensor,
+                                sin: torch.Tensor, window: int = -1, eps: float = 1e-6,
+                                layout: str = "bhtd"):
+    """Gradients (dq, dk, dv, dve, dgate_logits) of a layer with a value embedding, from the
+    gated v_work, out and lse of attn_fwd_qknorm_ve: the layer backward on v_work, then the
+    gate's backward (the gradient of v is that of v_work)."""
+    dq, dk, dv = attention_layer_backward(q, k, v_work, out, lse, dout, cos, sin, window, eps,
+                                          layout)
+    dve, dz = value_gate_bwd(ve, gate_logits, dv, layout=layout)
+    return dq, dk, dv, dve, dz
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            lengths: torch.Tensor | None = None, window: int = -1,
            out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
