@@ -148,6 +148,12 @@ def test_layer_with_value_embedding(d, B, H, H_kv, T, window, layout):
     torch.cuda.synchronize()
     assert torch.equal(vw, vg) and torch.equal(kw, kw2)
     assert torch.equal(out, o2) and torch.equal(lse, l2)
+    # in place: v_work = v, k_work = k
+    vi, ki = vd.clone(), kd.clone()
+    o3, l3, _, _ = ops.attn_fwd_qknorm_ve(qd, ki, vi, ved, zd, cos, sin, window=window,
+                                          k_work=ki, v_work=vi, layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(vi, vg) and torch.equal(ki, kw) and torch.equal(o3, out)
     ro, rl = oracle.attention_layer_ve(f64(q), f64(k), f64(v), f64(ve), f64(z), window=window)
     eo = float(np.max(np.abs(f64(from_layout(out, layout)) - ro)))
     el = float(np.max(np.abs(f64(lse) - rl)))
