@@ -121,3 +121,24 @@ def test_decode_validation_with_real_buffers():
                          ws.data_ptr(), 4096, 1, 2, 10, 64, -1, _lib.ATTN_BF16, None)
     assert rc == _lib.ATTN_OK
     torch.cuda.synchronize()
+
+
+def test_decode_long_cache():
+    """One step against a long cache: S = 131072 (d = 64, bf16, two kv heads shared by four query
+    heads), lengths at the cache's end, in its middle and of one token, full and windowed."""
+    B, H, H_kv, S, d = 3, 4, 2, 131072, 64
+    lengths = [S, S // 2 + 7, 1]
+    for window in (-1, 4096):
+        print(f"decode long cache S={S} window={window}", flush=True)
+        q = inputs.make_random((B, H, d), torch.bfloat16, 151)
+        k = inputs.make_random((B, H_kv, S, d), torch.bfloat16, 152)
+        v = inputs.make_random((B, H_kv, S, d), torch.bfloat16, 153)
+        ln = torch.tensor(lengths, dtype=torch.int32).cuda()
+        out, lse = ops.decode(q.cuda(), k.cuda(), v.cuda(), ln, window=window)
+        torch.cuda.synchronize()
+        f64 = lambda t: t.detach().cpu().to(torch.float64).numpy()
+        ro, rl = oracle.decode_attention(f64(q), f64(k), f64(v), lengths, window)
+        eo = float(np.max(np.abs(f64(out) - ro)))
+        el = float(np.max(np.abs(f64(lse) - rl)))
+        print(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+        assert eo <= 2e-2 and el <= 2e-2

@@ -310,3 +310,20 @@ def test_fused_validation_with_real_buffers():
     assert torch.all(out == 3.0) and torch.all(kw == 2.0)
     with pytest.raises(ValueError):
         ops.attn_fwd_qknorm(q.float(), k.float(), v.float(), cos, sin)
+
+
+@pytest.mark.parametrize("window", [4096, -1])
+def test_fused_long_single_head_sampled(window):
+    """A long sequence at the limits of one head: T = 131072 (d = 64, bf16, one batch entry and
+    two heads), window 4096 and full causal; the oracle checks sampled rows (the first, the
+    window's edge, block edges, the last)."""
+    B, H, T, d = 1, 2, 131072, 64
+    say(f"fused long single head T={T} d={d} W={window}")
+    q, k, v = (inputs.make_random((B, H, T, d), torch.bfloat16, s) for s in (141, 142, 143))
+    out, lse, _ = fused(q, k, v, window)
+    rng = np.random.default_rng(3)
+    fixed = {0, 1, 127, 128, 4095, 4096, 4097, T // 2, T - 129, T - 1}
+    rows = np.array(sorted(fixed | set(int(x) for x in rng.choice(T, 20, replace=False))))
+    for h in range(H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        check(out[sl], lse[sl], q[sl], k[sl], v[sl], window, rows=rows)
