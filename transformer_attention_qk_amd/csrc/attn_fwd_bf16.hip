@@ -786,15 +786,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kvoff, T * kv_rs);
   int tb, te;
   item_tiles<D, MODE>(q0, T, window, tb, te);
-  w.set_item(q0);
-  {
-    bf16x8 xf[C::KSTEPS];
-    typename WaveTile<D, MODE, QKN>::Rope rope;
-    w.load_q_global(head_rsrc(Q + hoff, T * q_rs), q0, xf);
-    w.load_rope(q0, cos_tab, sin_tab, rope);
-    w.set_q(xf, rope, q0, eps);
-  }
-
   auto gload = [&](__amdgpu_buffer_rsrc_t r, int t, bool needed, u32x4(&st)[C::LPT]) {
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
@@ -816,9 +807,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
     }
   };
 
+  // The item's Q rows, their rotation factors and its first K/V tile are all requested before
+  // the q norm waits for the first two, so the tile's latency overlaps theirs.
+  w.set_item(q0);
   u32x4 kst[C::LPT], vst[C::LPT];
-  gload(rk, tb, true, kst);
-  gload(rv, tb, true, vst);
+  {
+    bf16x8 xf[C::KSTEPS];
+    typename WaveTile<D, MODE, QKN>::Rope rope;
+    w.load_q_global(head_rsrc(Q + hoff, T * q_rs), q0, xf);
+    w.load_rope(q0, cos_tab, sin_tab, rope);
+    gload(rk, tb, true, kst);
+    gload(rv, tb, true, vst);
+    w.set_q(xf, rope, q0, eps);
+  }
+
   lstore(0, kst, vst);
   __syncthreads();
   for (int t = tb; t < te; ++t) {
