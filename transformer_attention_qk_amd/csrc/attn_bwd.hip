@@ -29,6 +29,8 @@
 // fp32; dQ, dK, dV are rounded to bf16 once at the end.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_ops.hpp"
@@ -186,11 +188,14 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const Elem* __restr
 // ---------------------------------------------------------------------------------------------
 // dK, dV (bf16 MFMA).
 // ---------------------------------------------------------------------------------------------
-// Two workgroups per CU (two waves per SIMD) where the registers allow it, d <= 64: a wave's
-// chain of loads, MFMAs and exponentials leaves the SIMD idle between its own instructions, and
-// the second wave fills those gaps. d = 128's accumulators need the whole register file.
-template <int D, int MODE>
-__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
+// Two workgroups per CU (two waves per SIMD): a wave's chain of loads, MFMAs and exponentials
+// leaves the SIMD idle between its own instructions, and the second wave fills those gaps.
+// PASS selects the outputs: kBothPasses computes dK and dV together (d <= 64); at d = 128 the two
+// accumulator sets do not fit two waves' registers, so one launch computes dV (S and P only) and
+// a second dK (S, dP and dS): S is computed twice, a quarter more MFMA work for twice the waves.
+constexpr int kBothPasses = 2, kPassDV = 0, kPassDK = 1;
+template <int D, int MODE, int PASS>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, Geometry geo, int H_kv, int T, int window_arg,
@@ -222,12 +227,13 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
   // 16 s + 8 (l / 32) .. + 8.
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + kvoff, T * kv_rs);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + kvoff, T * kv_rs);
-  bf16x8 kf[C::KS], vf[C::KS];
+  constexpr bool DO_DV = PASS != kPassDK, DO_DK = PASS != kPassDV;
+  bf16x8 kf[C::KS], vf[C::KS];  // vf: only where dP is needed (dK)
 #pragma unroll
   for (int s = 0; s < C::KS; ++s) {
     const uint32_t off = (uint32_t)((kw0 + l32) * kv_rs + 32 * s + 16 * hi);
     kf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off));
-    vf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rv, off));
+    if constexpr (DO_DK) vf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rv, off));
   }
   f32x16 dka[C::DB], dva[C::DB];
 #pragma unroll
@@ -279,34 +285,36 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
   };
   // Scores S = Q K^T and dP = dO V^T of the tile in buffer `buf`, both 32-query halves (four
   // independent MFMA chains).
-  auto scores2 = [&](int buf, f32x16(&sa)[2], f32x16(&dp)[2]) {
+  auto scores2 = [&](int buf, f32x16(&sa)[2], f32x16(&dp)[2], int s0, int s1) {
     const char* qtile = smem + buf * BUF;
     const char* dotile = qtile + C::TILE_BYTES;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = s0; sub < s1; ++sub) {
       sa[sub] = f32x16{};
       dp[sub] = f32x16{};
     }
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = s0; sub < s1; ++sub) {
         sa[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tile_row16<D>(qtile, 32 * sub + l32, 2 * s + hi), kf[s], sa[sub], 0, 0, 0);
-        dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tile_row16<D>(dotile, 32 * sub + l32, 2 * s + hi), vf[s], dp[sub], 0, 0, 0);
+        if constexpr (DO_DK)
+          dp[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tile_row16<D>(dotile, 32 * sub + l32, 2 * s + hi), vf[s], dp[sub], 0, 0, 0);
       }
     }
   };
   // P and dS of the tile at query qt in buffer `buf` from its scores, then dV^T += dO^T P and
   // dK^T += Q^T dS. A half this wave does not see is masked to zero weights.
-  auto grads = [&](int buf, int qt, const f32x16(&sa)[2], const f32x16(&dp)[2]) {
+  auto grads = [&](int buf, int qt, const f32x16(&sa)[2], const f32x16(&dp)[2], int s0,
+                   int s1) {
     const char* qtile = smem + buf * BUF;
     const char* dotile = qtile + C::TILE_BYTES;
     const float* lse_s = reinterpret_cast<const float*>(qtile + 2 * C::TILE_BYTES);
     const float* del_s = lse_s + C::TR;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = s0; sub < s1; ++sub) {
       const int qs = qt + 32 * sub;
       // Register r: query qs + acc_row(r); lane: key kw0 + l32.
       const bool all = block_all<MODE>(qs, kw0, T, window);
@@ -314,14 +322,15 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 32 * sub + 8 * gq + 4 * hi);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + 32 * sub + 8 * gq + 4 * hi);
+        f32x4 d4 = f32x4{};
+        if constexpr (DO_DK) d4 = *reinterpret_cast<const f32x4*>(del_s + 32 * sub + 8 * gq + 4 * hi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
           float pr = __builtin_amdgcn_exp2f(fmaf(sa[sub][r], scale_log2, -l4[e]));
           if (!all) pr = visible_qk<MODE>(qs + acc_row(r, hi), key, T, window) ? pr : 0.f;
           p[r] = pr;
-          ds[r] = pr * (dp[sub][r] - d4[e]);
+          if constexpr (DO_DK) ds[r] = pr * (dp[sub][r] - d4[e]);
         }
       }
 #pragma unroll
@@ -329,17 +338,19 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
         u32x4 pw, dw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pw[e] = pack_bf16x2(p[8 * tt + 2 * e], p[8 * tt + 2 * e + 1]);
-          dw[e] = pack_bf16x2(ds[8 * tt + 2 * e], ds[8 * tt + 2 * e + 1]);
+          if constexpr (DO_DV) pw[e] = pack_bf16x2(p[8 * tt + 2 * e], p[8 * tt + 2 * e + 1]);
+          if constexpr (DO_DK) dw[e] = pack_bf16x2(ds[8 * tt + 2 * e], ds[8 * tt + 2 * e + 1]);
         }
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
         const bf16x8 dsb = __builtin_bit_cast(bf16x8, dw);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tile_tr16<D>(dotile, 32 * sub + 16 * tt, db, lane), pb, dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tile_tr16<D>(qtile, 32 * sub + 16 * tt, db, lane), dsb, dka[db], 0, 0, 0);
+          if constexpr (DO_DV)
+            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                tile_tr16<D>(dotile, 32 * sub + 16 * tt, db, lane), pb, dva[db], 0, 0, 0);
+          if constexpr (DO_DK)
+            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                tile_tr16<D>(qtile, 32 * sub + 16 * tt, db, lane), dsb, dka[db], 0, 0, 0);
         }
       }
     }
@@ -360,8 +371,16 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
     if (i + 1 < n_tiles) fetch(i + 1);
     if (seen(i)) {
       f32x16 sa[2], dp[2];
-      scores2(i & 1, sa, dp);
-      grads(i & 1, qt_of(i), sa, dp);
+      if constexpr (PASS == kPassDK) {
+        // one 32-query half at a time: the registers of a second half's S and dP are not there
+        scores2(i & 1, sa, dp, 0, 1);
+        grads(i & 1, qt_of(i), sa, dp, 0, 1);
+        scores2(i & 1, sa, dp, 1, 2);
+        grads(i & 1, qt_of(i), sa, dp, 1, 2);
+      } else {
+        scores2(i & 1, sa, dp, 0, 2);
+        grads(i & 1, qt_of(i), sa, dp, 0, 2);
+      }
     }
     if (i + 1 < n_tiles) put((i + 1) & 1);
     __syncthreads();
@@ -380,8 +399,8 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void attn_bwd_dkdv_bf16(
         wk[1] = pack_bf16x2(dka[db][4 * gq + 2] * scale, dka[db][4 * gq + 3] * scale);
         wv[0] = pack_bf16x2(dva[db][4 * gq], dva[db][4 * gq + 1]);
         wv[1] = pack_bf16x2(dva[db][4 * gq + 2], dva[db][4 * gq + 3]);
-        *reinterpret_cast<u32x2*>(krow + 32 * db + 8 * gq + 4 * hi) = wk;
-        *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * gq + 4 * hi) = wv;
+        if constexpr (DO_DK) *reinterpret_cast<u32x2*>(krow + 32 * db + 8 * gq + 4 * hi) = wk;
+        if constexpr (DO_DV) *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * gq + 4 * hi) = wv;
       }
     }
   }
@@ -630,12 +649,23 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
   const float scale = (float)(1.0 / sqrt((double)D));
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   const int nkb = (dm.T + 127) / 128;
-  hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, MODE>), dim3((unsigned)(dm.B * dm.H_kv * nkb)),
-                     dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                     (const bf16*)dout, lse, delta, (bf16*)dk, (bf16*)dv, geo, dm.H_kv, dm.T,
-                     window, scale_log2, scale, nkb,
-                     group_heads(dm.B * dm.H_kv, (int64_t)dm.T * D * 2 * 2));
-  hipError_t e = hipGetLastError();
+  const int gh = group_heads(dm.B * dm.H_kv, (int64_t)dm.T * D * 2 * 2);
+  auto dkdv = [&](auto pass_c) {
+    constexpr int PASS = decltype(pass_c)::value;
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16<D, MODE, PASS>),
+                       dim3((unsigned)(dm.B * dm.H_kv * nkb)), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
+                       delta, (bf16*)dk, (bf16*)dv, geo, dm.H_kv, dm.T, window, scale_log2, scale,
+                       nkb, gh);
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if constexpr (D <= 64) {
+    e = dkdv(std::integral_constant<int, kBothPasses>{});
+  } else {
+    e = dkdv(std::integral_constant<int, kPassDV>{});
+    if (e == hipSuccess) e = dkdv(std::integral_constant<int, kPassDK>{});
+  }
   if (e != hipSuccess) return e;
   const int BH = dm.B * dm.H;
   hipLaunchKernelGGL((attn_bwd_dq_bf16<D, MODE>), dim3((unsigned)(BH * nkb)), dim3(256), 0,
