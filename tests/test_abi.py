@@ -608,10 +608,17 @@ def test_value_gate_bwd_rejects_before_any_hip_call(lib, name, kw, code):
 # ---------------------------------------------------------------------------------------------
 
 def test_decode_workspace_bytes(lib):
-    # B * H * ceil(keys / 128) * (d + 2) * 4, keys = min(S, window + 1)
-    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, -1) == 2 * 3 * 8 * 66 * 4
-    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, 127) == 2 * 3 * 1 * 66 * 4
-    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, 128) == 2 * 3 * 2 * 66 * 4
+    # B * H * splits * (d + 2) * 4 with keys = min(S, window + 1) and
+    # splits = min(ceil(keys / (4 * 4096 / d)), ceil(2048 / (B * H))): 256 keys per split at
+    # d = 64, 128 at d = 128, 1024 at d = 16, and about 2048 workgroups at most
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, -1) == 2 * 3 * 4 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, 255) == 2 * 3 * 1 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 64, 256) == 2 * 3 * 2 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(2, 3, 1000, 128, -1) == 2 * 3 * 8 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(2, 3, 1025, 16, -1) == 2 * 3 * 2 * 18 * 4
+    assert lib.attn_decode_workspace_bytes(1, 1, 1 << 20, 64, -1) == 2048 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(1, 16, 131072, 128, -1) == 16 * 128 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(64, 64, 4096, 128, -1) == 64 * 64 * 1 * 130 * 4
     assert lib.attn_decode_workspace_bytes(0, 3, 1000, 64, -1) == -1
     assert lib.attn_decode_workspace_bytes(1, 1, 1, 64, -2) == -1
 
@@ -639,7 +646,7 @@ DEC_CASES = [
     ("window -2", dict(window=-2), _lib.ATTN_ERR_WINDOW),
     ("misaligned out", dict(out=_DC["out"] + 8), _lib.ATTN_ERR_ALIGN),
     ("misaligned lengths", dict(len=_DC["len"] + 2), _lib.ATTN_ERR_ALIGN),
-    ("workspace too small", dict(wsb=2 * 4 * 3 * 66 * 4 - 4), _lib.ATTN_ERR_ARG),
+    ("workspace too small", dict(wsb=2 * 4 * 2 * 66 * 4 - 4), _lib.ATTN_ERR_ARG),
     ("out is q", dict(out=_DC["q"]), _lib.ATTN_ERR_ALIAS),
     ("workspace inside k", dict(ws=_DC["k"] + 4096), _lib.ATTN_ERR_ALIAS),
     ("lse inside workspace", dict(lse=_DC["ws"] + 16), _lib.ATTN_ERR_ALIAS),

@@ -47,6 +47,11 @@ for _d in (32, 64, 128):
 for _d in (16, 64, 128):
     CASES += [("f32", _d, 2, 4, 2, 150, [150, 3], -1, "bhtd"), ("f32", _d, 2, 2, 2, 90, None, 5, "bthd")]
 CASES += [("bf16", 64, 2, 24, 2, 700, [700, 1], -1, "bhtd")]  # 12 query heads per kv head
+# Long caches over few heads: the splits are capped, so each wave takes several batches of rows
+# (with GQA: re-read for every query head of the group).
+CASES += [("bf16", 128, 2, 8, 2, 40000, [40000, 12345], -1, "bhtd"),
+          ("bf16", 64, 1, 8, 8, 100000, [99999], 70000, "bthd"),
+          ("f32", 128, 1, 4, 2, 70000, None, -1, "bhtd")]
 
 
 @pytest.mark.parametrize("dt,d,B,H,H_kv,S,lengths,window,layout", CASES,

@@ -530,7 +530,8 @@ int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, cons
     for (int o = 0; o < 7; ++o)
       if (o != w && bufs[o] && overlap(bufs[w], len[w], bufs[o], len[o])) return ATTN_ERR_ALIAS;
   }
-  if ((int64_t)B * H_kv * attn::decode_splits(S, window) > kMaxGrid) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * H_kv * attn::decode_splits(B, H, S, d, window) > kMaxGrid)
+    return ATTN_ERR_SHAPE;
   const hipError_t e = attn::launch_attn_decode(q, k_cache, v_cache, lengths, out, lse, workspace,
                                                 dm, window, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

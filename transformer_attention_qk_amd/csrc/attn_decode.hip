@@ -6,11 +6,15 @@
 //   out = sum_j softmax_j(q . k_j / sqrt(d)) v_j,   lse = ln sum_j exp(q . k_j / sqrt(d)).
 //
 // A single query row is a matrix-vector product, bound by reading the cache (4 d bytes per key
-// in bf16), so the work is split over the keys: one workgroup per (batch, kv head, chunk of 128
-// keys) stages its chunk of K and V in LDS with coalesced 16-byte loads, then for every query
-// head of the group forms the chunk's scores (fp32), its maximum m, weights exp2(s - m) and
-// their sum l, and the weighted sum of the V rows, written unnormalised with m and l to the
-// caller's workspace. A merge kernel combines the chunks of each (batch, head):
+// in bf16), so the work is split over the keys, and what keeps the reads near the HBM rate is how
+// many bytes each wave has in flight. A workgroup takes (batch, kv head, split of the keys); each
+// of its four waves loads its own 4096 / d rows of K and of V straight into registers (16 KB in
+// bf16, every load issued before the first use) and, for every query head of the group (GQA: the
+// cache is read once for the whole group), forms the scores (fp32), their maximum m, the weights
+// exp2(s - m), their sum l and the weighted sum of the V rows with shuffles inside the wave only.
+// The four waves' (m, l, o) meet in LDS, one barrier per query head, and the workgroup writes its
+// split's o, unnormalised, with m and l to the caller's workspace. A merge kernel combines the
+// splits of each (batch, head):
 //   M = max_c m_c,  L = sum_c l_c 2^(m_c - M),  out = sum_c o_c 2^(m_c - M) / L,
 //   lse = (M + log2 L) ln 2.
 // The weights stay fp32 (no bf16 rounding), every sum is fp32, out is rounded once.
@@ -21,20 +25,25 @@
 
 namespace attn {
 
-constexpr int kDecodeChunk = 128;  // keys per workgroup
-constexpr int kDecodeHeads = 4;    // query heads per pass over a staged chunk
+constexpr int kDecodeWaves = 4;  // waves per workgroup, each with its own rows
+
+// Keys per wave and batch: 4096 / d rows of K and of V, i.e. 8 (bf16) or 16 (fp32) 16-byte
+// loads per lane and tensor. A split of the keys is one workgroup's four waves: one batch each
+// while that gives at most kDecodeTargetGroups workgroups, else fewer splits with several batches
+// per wave (long caches), which keeps the merge short.
+constexpr int decode_wave_keys(int d) { return d >= 4096 ? 1 : 4096 / d; }
+constexpr int decode_split_keys(int d) { return kDecodeWaves * decode_wave_keys(d); }
+constexpr int kDecodeTargetGroups = 2048;
 
 template <typename Elem, int D>
 struct DecCfg {
-  static constexpr int CK = kDecodeChunk;
-  static constexpr int HB = kDecodeHeads;
-  static constexpr int E = 16 / (int)sizeof(Elem);          // elements per 16-byte chunk
-  static constexpr int CHR = D / E;                          // 16-byte chunks per row
-  static constexpr int ROWB = D * (int)sizeof(Elem) + 16;    // padded LDS row (bank spread)
-  static constexpr int V_BYTES = CK * ROWB;
-  static_assert(CK <= 128, "two threads per key: a chunk holds at most 128 keys");
-  static constexpr int RED = 4 * HB * D * 4;  // per-wave partial sums of the outputs
-  static constexpr int LDS = V_BYTES + HB * D * 4 + HB * CK * 4 + 2 * HB * 4 + RED;
+  static constexpr int E = 16 / (int)sizeof(Elem);  // elements per 16-byte chunk
+  static constexpr int CHR = D / E;                  // lanes per row: one chunk each
+  static constexpr int RPL = 64 / CHR;               // rows covered by one load of a wave
+  static constexpr int KW = decode_wave_keys(D);     // rows per wave
+  static constexpr int NL = KW / RPL;                // loads per lane and tensor
+  static_assert(CHR >= 1 && CHR <= 64 && 64 % CHR == 0, "a row must span a power of two lanes");
+  static_assert(NL >= 1 && NL * RPL == KW, "rows per wave must be whole loads");
 };
 
 template <typename Elem>
@@ -57,18 +66,14 @@ __device__ __forceinline__ void chunk_f32(u32x4 w, float (&x)[16 / sizeof(Elem)]
 }
 
 template <typename Elem, int D>
-__global__ __launch_bounds__(256, 2) void attn_decode_partial(
+__global__ __launch_bounds__(256) void attn_decode_partial(
     const Elem* __restrict__ Qv, const Elem* __restrict__ K, const Elem* __restrict__ V,
     const int* __restrict__ lengths, float* __restrict__ ws, Geometry geo, int H_kv, int S,
     int window, int n_split, int64_t parts, float scale_log2) {
   using C = DecCfg<Elem, D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* vs = smem;
-  float* qs = reinterpret_cast<float*>(smem + C::V_BYTES);        // [HB][D]
-  float* ss = qs + C::HB * D;                                     // [HB][CK]
-  float* ms = ss + C::HB * C::CK;                                 // [HB]
-  float* ls = ms + C::HB;                                         // [HB]
-  float* red = ls + C::HB;                                        // [4 waves][HB][D]
+  // Per query head (two heads alternate, so one barrier per head suffices): each wave's
+  // unnormalised o[D], then its m and l.
+  __shared__ float red[2][kDecodeWaves][D + 2];
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = (int)blockIdx.x % n_split;
   const int bg = (int)blockIdx.x / n_split;
@@ -77,212 +82,200 @@ __global__ __launch_bounds__(256, 2) void attn_decode_partial(
   int n = (lengths != nullptr) ? lengths[b] : S;
   n = min(max(n, 1), S);
   const int lo = (window >= 0) ? max(0, n - 1 - window) : 0;
-  const int c0 = lo + split * C::CK;
-  const int cnt = min(n, c0 + C::CK) - c0;  // keys of this chunk (block-uniform; may be <= 0)
+  // The entry's keys [lo, n) in n_split equal splits, each in four equal parts, one per wave;
+  // a wave takes its part in batches of KW rows. Parts past n are empty.
+  const int per_split = (n - lo + n_split - 1) / n_split;
+  const int s0 = lo + split * per_split;
+  const int s1 = min(n, s0 + per_split);
+  const int per_wave = (per_split + kDecodeWaves - 1) / kDecodeWaves;
+  const int w0 = s0 + wave * per_wave;
+  const int cnt = min(s1, w0 + per_wave) - w0;  // rows of this wave (wave-uniform; may be <= 0)
   // Workspace: unnormalised outputs [B][H][n_split][D], then m and l [B][H][n_split].
   float* ws_o = ws;
   float* ws_m = ws + parts * D;
   float* ws_l = ws_m + parts;
 
-  if (cnt <= 0) {  // an empty chunk (short entry): weight 0 in the merge
-    for (int idx = tid; idx < G * D; idx += 256) {
-      const int hh = idx / D, e = idx - hh * D;
-      const int64_t part = ((int64_t)b * H + g * G + hh) * n_split + split;
-      ws_o[part * D + e] = 0.f;
-      if (e == 0) {
-        ws_m[part] = -INFINITY;
-        ws_l[part] = 0.f;
-      }
-    }
-    return;
-  }
-
-  // Threads 2 j and 2 j + 1 hold the two halves of key j's row in registers (the reads of a wave
-  // cover 32 consecutive rows); the V rows are staged in LDS. Every load is issued before the
-  // first store, so their latencies overlap.
+  // Lane l holds chunk c = l % CHR of rows rl + RPL u (u < NL) of a batch, so the reads of one
+  // load cover RPL consecutive rows.
   const int64_t kvoff = (int64_t)b * geo.kv.b + (int64_t)g * geo.kv.h;
-  const int kj = tid >> 1, half = tid & 1;
-  const bool live = kj < cnt;
-  u32x4 kr[C::CHR / 2];
-  if (live) {
-    const Elem* krow = K + kvoff + (int64_t)(c0 + kj) * geo.kv.t + half * (D / 2);
+  const int rl = lane / C::CHR, c = lane % C::CHR;
+  u32x4 kr[C::NL], vr[C::NL];
+  auto load_batch = [&](int r0) {
 #pragma unroll
-    for (int c = 0; c < C::CHR / 2; ++c) kr[c] = *reinterpret_cast<const u32x4*>(krow + c * C::E);
-  }
-  {
-    constexpr int LPT = (C::CK * C::CHR + 255) / 256;
-    u32x4 xv[LPT];
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int p = u * 256 + tid;
-      const int r = p / C::CHR, c = p - r * C::CHR;
-      if (r < cnt)
-        xv[u] = *reinterpret_cast<const u32x4*>(V + kvoff + (int64_t)(c0 + r) * geo.kv.t + c * C::E);
+    for (int u = 0; u < C::NL; ++u) {
+      const int r = r0 + u * C::RPL + rl;
+      kr[u] = u32x4{0u, 0u, 0u, 0u};
+      vr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (r < cnt) {
+        const int64_t off = kvoff + (int64_t)(w0 + r) * geo.kv.t + c * C::E;
+        kr[u] = *reinterpret_cast<const u32x4*>(K + off);
+        vr[u] = *reinterpret_cast<const u32x4*>(V + off);
+      }
     }
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int p = u * 256 + tid;
-      const int r = p / C::CHR, c = p - r * C::CHR;
-      if (r < cnt) *reinterpret_cast<u32x4*>(vs + r * C::ROWB + 16 * c) = xv[u];
-    }
-  }
-  if (!live) {
-#pragma unroll
-    for (int c = 0; c < C::CHR / 2; ++c) kr[c] = u32x4{0u, 0u, 0u, 0u};
-  }
+  };
+  load_batch(0);  // before the query is read, so the cache reads go out first
 
-  for (int hb0 = 0; hb0 < G; hb0 += C::HB) {
-    const int nh = min(C::HB, G - hb0);
-    __syncthreads();  // the chunk is staged; the previous pass is done with qs, ss
-    for (int idx = tid; idx < nh * D; idx += 256) {
-      const int hh = idx / D, e = idx - hh * D;
-      qs[hh * D + e] = elem_f32(Qv[((int64_t)b * H + g * G + hb0 + hh) * D + e]);
-    }
-    __syncthreads();
-    // Scores: threads 2 j and 2 j + 1 take the two halves of key j's dot product with each head.
-    for (int hh = 0; hh < nh; ++hh) {
-      float acc = 0.f;
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    float qv[C::E];
+    chunk_f32<Elem>(*reinterpret_cast<const u32x4*>(Qv + ((int64_t)b * H + h) * D + c * C::E), qv);
+    // Running maximum m (base-2 units), sum l and this lane's chunk of the weighted V sum over the
+    // wave's batches (one-pass softmax; the first batch sets m).
+    float m = -INFINITY, l = 0.f, acc[C::E];
 #pragma unroll
-      for (int c = 0; c < C::CHR / 2; ++c) {
+    for (int e = 0; e < C::E; ++e) acc[e] = 0.f;
+    for (int r0 = 0; r0 < cnt; r0 += C::KW) {
+      // The registers hold the first batch for the first head, and for every head when the
+      // part is one batch.
+      if (r0 > 0 || (hh > 0 && cnt > C::KW)) load_batch(r0);
+      // Scores: this lane's part of each row's dot product, summed over the row's CHR lanes;
+      // rows past the part are -inf.
+      float sc[C::NL];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < C::NL; ++u) {
         float y[C::E];
-        chunk_f32<Elem>(kr[c], y);
+        chunk_f32<Elem>(kr[u], y);
+        float a = 0.f;
 #pragma unroll
-        for (int e = 0; e < C::E; ++e)
-          acc = fmaf(qs[hh * D + half * (D / 2) + c * C::E + e], y[e], acc);
+        for (int e = 0; e < C::E; ++e) a = fmaf(qv[e], y[e], a);
+#pragma unroll
+        for (int o = 1; o < C::CHR; o <<= 1) a += __shfl_xor(a, o);
+        sc[u] = (r0 + u * C::RPL + rl < cnt) ? a * scale_log2 : -INFINITY;
+        mb = fmaxf(mb, sc[u]);
       }
-      acc += __shfl_xor(acc, 1);
-      if (half == 0 && kj < C::CK) ss[hh * C::CK + kj] = live ? acc * scale_log2 : -INFINITY;
-    }
-    __syncthreads();
-    // Per head: maximum, weights, their sum (one wave per head).
-    for (int hh = wave; hh < nh; hh += 4) {
-      float m = -INFINITY;
-      for (int j = lane; j < C::CK; j += 64) m = fmaxf(m, ss[hh * C::CK + j]);
+      // The lanes of a row share its score, so the wave's reductions cross the row groups only.
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      float l = 0.f;
-      for (int j = lane; j < C::CK; j += 64) {
-        const float p = (j < cnt) ? __builtin_amdgcn_exp2f(ss[hh * C::CK + j] - m) : 0.f;
-        ss[hh * C::CK + j] = p;
-        l += p;
-      }
+      for (int o = C::CHR; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
+      const float mn = fmaxf(m, mb);              // finite: the batch has a row
+      const float f = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first batch
+      float lb = 0.f;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-      if (lane == 0) {
-        ms[hh] = m;
-        ls[hh] = l;
-      }
-    }
-    __syncthreads();
-    // Weighted sum of the V rows: thread t takes the 16-byte chunk c = t % CHR of the rows of
-    // key group kg = t / CHR (keys kg, kg + NKG, ...); the key groups of a wave meet through xor
-    // shuffles, the four waves' sums in LDS.
-    {
-      constexpr int NKG = 256 / C::CHR;
-      const int c = tid % C::CHR, kg = tid / C::CHR;
-      float acc[C::HB][C::E];
+      for (int e = 0; e < C::E; ++e) acc[e] *= f;
 #pragma unroll
-      for (int hh = 0; hh < C::HB; ++hh)
-#pragma unroll
-        for (int e = 0; e < C::E; ++e) acc[hh][e] = 0.f;
-#pragma unroll 4
-      for (int j = kg; j < cnt; j += NKG) {
+      for (int u = 0; u < C::NL; ++u) {
+        const float p = __builtin_amdgcn_exp2f(sc[u] - mn);  // 0 for rows past the part
+        lb += p;
         float y[C::E];
-        chunk_f32<Elem>(*reinterpret_cast<const u32x4*>(vs + j * C::ROWB + 16 * c), y);
+        chunk_f32<Elem>(vr[u], y);
 #pragma unroll
-        for (int hh = 0; hh < C::HB; ++hh) {
-          const float pj = (hh < nh) ? ss[hh * C::CK + j] : 0.f;
+        for (int e = 0; e < C::E; ++e) acc[e] = fmaf(p, y[e], acc[e]);
+      }
+      l = fmaf(l, f, lb);
+      m = mn;
+    }
+    // Sums over the row groups (acc and l are per lane until here; m is already the wave's).
 #pragma unroll
-          for (int e = 0; e < C::E; ++e) acc[hh][e] = fmaf(pj, y[e], acc[hh][e]);
+    for (int o = C::CHR; o < 64; o <<= 1) {
+      l += __shfl_xor(l, o);
+#pragma unroll
+      for (int e = 0; e < C::E; ++e) acc[e] += __shfl_xor(acc[e], o);
+    }
+    float* rw = red[hh & 1][wave];
+    if (rl == 0) {
+#pragma unroll
+      for (int e = 0; e < C::E; ++e) rw[c * C::E + e] = acc[e];
+    }
+    if (lane == 0) {
+      rw[D] = m;
+      rw[D + 1] = l;
+    }
+    __syncthreads();
+    // The split's (m, l, o) from its waves' (empty parts: l = 0, weight 0).
+    if (tid < D) {
+      float (*rp)[D + 2] = red[hh & 1];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w)
+        if (rp[w][D + 1] > 0.f) M = fmaxf(M, rp[w][D]);
+      float L = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float lw = rp[w][D + 1];
+        if (lw > 0.f) {
+          const float fw = __builtin_amdgcn_exp2f(rp[w][D] - M);
+          L = fmaf(lw, fw, L);
+          o = fmaf(rp[w][tid], fw, o);
         }
       }
-#pragma unroll
-      for (int o = C::CHR; o < 64; o <<= 1)
-#pragma unroll
-        for (int hh = 0; hh < C::HB; ++hh)
-#pragma unroll
-          for (int e = 0; e < C::E; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], o);
-      if (lane < C::CHR) {
-#pragma unroll
-        for (int hh = 0; hh < C::HB; ++hh)
-#pragma unroll
-          for (int e = 0; e < C::E; ++e) red[(wave * C::HB + hh) * D + c * C::E + e] = acc[hh][e];
-      }
-      __syncthreads();
-      for (int idx = tid; idx < nh * D; idx += 256) {
-        const int hh = idx / D, ee = idx - hh * D;
-        const float o = red[(0 * C::HB + hh) * D + ee] + red[(1 * C::HB + hh) * D + ee] +
-                        red[(2 * C::HB + hh) * D + ee] + red[(3 * C::HB + hh) * D + ee];
-        const int64_t part = ((int64_t)b * H + g * G + hb0 + hh) * n_split + split;
-        ws_o[part * D + ee] = o;
-        if (ee == 0) {
-          ws_m[part] = ms[hh];
-          ws_l[part] = ls[hh];
-        }
+      const int64_t part = ((int64_t)b * H + h) * n_split + split;
+      ws_o[part * D + tid] = o;
+      if (tid == 0) {
+        ws_m[part] = M;
+        ws_l[part] = L;
       }
     }
   }
 }
 
+// One block of 256 threads per (batch, head): thread (e, cg) folds output element e over the
+// splits c = cg, cg + NG, ... (NG = 256 / D) in one pass with a running maximum, then the NG
+// partial results meet in LDS.
 template <typename Elem, int D>
-__global__ __launch_bounds__(128) void attn_decode_merge(const float* __restrict__ ws,
+__global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict__ ws,
                                                          Elem* __restrict__ out,
                                                          float* __restrict__ lse, int n_split,
                                                          int64_t parts) {
-  __shared__ float red[2][2];
-  const int bh = (int)blockIdx.x, tid = (int)threadIdx.x, nt = (int)blockDim.x;
+  constexpr int NG = 256 / D;
+  __shared__ float sm[3][NG][D];
+  const int bh = (int)blockIdx.x, tid = (int)threadIdx.x;
+  const int e = tid % D, cg = tid / D;
   const float* ws_m = ws + parts * D + (int64_t)bh * n_split;
-  const float* ws_l = ws + parts * D + parts + (int64_t)bh * n_split;
+  const float* ws_l = ws_m + parts;
   const float* ws_o = ws + (int64_t)bh * n_split * D;
-  // M = max_c m_c and L = sum_c l_c 2^(m_c - M) over the chunks (empty chunks: l = 0), reduced
-  // over the block (at most two waves).
-  auto block_reduce = [&](float x, bool is_max) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float y = __shfl_xor(x, o);
-      x = is_max ? fmaxf(x, y) : x + y;
+  // Empty splits (l = 0, m = -inf, o = 0) get weight 0.
+  float M = -INFINITY, L = 0.f, o = 0.f;
+#pragma unroll 8
+  for (int c = cg; c < n_split; c += NG) {
+    const float lc = ws_l[c], mc = ws_m[c], oc = ws_o[(int64_t)c * D + e];
+    if (lc > 0.f) {
+      const float mn = fmaxf(M, mc);
+      const float f = __builtin_amdgcn_exp2f(M - mn), w = __builtin_amdgcn_exp2f(mc - mn);
+      L = fmaf(L, f, lc * w);
+      o = fmaf(o, f, oc * w);
+      M = mn;
     }
-    if ((tid & 63) == 0) red[is_max][tid >> 6] = x;
-    __syncthreads();
-    const int nw = (nt + 63) / 64;
-    float r = red[is_max][0];
-    for (int w = 1; w < nw; ++w) r = is_max ? fmaxf(r, red[is_max][w]) : r + red[is_max][w];
-    return r;
-  };
-  float m = -INFINITY;
-  for (int c = tid; c < n_split; c += nt) m = fmaxf(m, ws_m[c]);
-  const float M = block_reduce(m, true);
-  float l = 0.f;
-  for (int c = tid; c < n_split; c += nt)
-    l += (ws_l[c] > 0.f) ? ws_l[c] * __builtin_amdgcn_exp2f(ws_m[c] - M) : 0.f;
-  const float L = block_reduce(l, false);
-  const float inv = 1.0f / L;
-  for (int e = tid; e < D; e += nt) {
-    float o = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < n_split; ++c) {
-      const float w = (ws_l[c] > 0.f) ? __builtin_amdgcn_exp2f(ws_m[c] - M) : 0.f;
-      o = fmaf(ws_o[(int64_t)c * D + e], w, o);
-    }
-    out[(int64_t)bh * D + e] = (Elem)(o * inv);
   }
-  if (tid == 0 && lse != nullptr) lse[bh] = (M + __log2f(L)) * kLn2;
+  sm[0][cg][e] = M;
+  sm[1][cg][e] = L;
+  sm[2][cg][e] = o;
+  __syncthreads();
+  if (cg == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (sm[1][i][e] > 0.f) Mt = fmaxf(Mt, sm[0][i][e]);
+    float Lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (sm[1][i][e] > 0.f) {
+        const float w = __builtin_amdgcn_exp2f(sm[0][i][e] - Mt);
+        Lt = fmaf(sm[1][i][e], w, Lt);
+        ot = fmaf(sm[2][i][e], w, ot);
+      }
+    }
+    out[(int64_t)bh * D + e] = (Elem)(ot * (1.0f / Lt));
+    if (e == 0 && lse != nullptr) lse[bh] = (Mt + __log2f(Lt)) * kLn2;
+  }
 }
 
-int decode_splits(int S, int window) {
+int decode_splits(int B, int H, int S, int d, int window) {
   const int keys = (window >= 0 && window + 1 < S) ? window + 1 : S;
-  return (keys + kDecodeChunk - 1) / kDecodeChunk;
+  const int64_t by_keys = (keys + decode_split_keys(d) - 1) / decode_split_keys(d);
+  const int64_t heads = (int64_t)B * H;
+  const int64_t cap = (kDecodeTargetGroups + heads - 1) / heads;
+  return (int)(by_keys < cap ? by_keys : cap);
 }
 
 int64_t decode_workspace_bytes(int B, int H, int S, int d, int window) {
-  return (int64_t)B * H * decode_splits(S, window) * (d + 2) * 4;
+  return (int64_t)B * H * decode_splits(B, H, S, d, window) * (d + 2) * 4;
 }
 
 template <typename Elem, int D>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const int* lengths,
                                   void* out, float* lse, void* ws, const Dims& dm, int window,
                                   hipStream_t stream) {
-  const int n_split = decode_splits(dm.T, window);
+  const int n_split = decode_splits(dm.B, dm.H, dm.T, D, window);
   const int64_t parts = (int64_t)dm.B * dm.H * n_split;
   const Geometry geo = make_geometry(dm);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -291,9 +284,8 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
                      (float*)ws, geo, dm.H_kv, dm.T, window, n_split, parts, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_merge<Elem, D>), dim3((unsigned)(dm.B * dm.H)),
-                     dim3(D < 128 ? D : 128), 0, stream, (const float*)ws, (Elem*)out, lse,
-                     n_split, parts);
+  hipLaunchKernelGGL((attn_decode_merge<Elem, D>), dim3((unsigned)(dm.B * dm.H)), dim3(256), 0,
+                     stream, (const float*)ws, (Elem*)out, lse, n_split, parts);
   return hipGetLastError();
 }
 

@@ -111,7 +111,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
 
 // Decode: one query per (batch, head) against a cache of dm.T slots (lengths: device int32 [B]
 // or nullptr for all dm.T). ws: decode_workspace_bytes(...) bytes of device memory.
-int decode_splits(int S, int window);
+int decode_splits(int B, int H, int S, int d, int window);
 int64_t decode_workspace_bytes(int B, int H, int S, int d, int window);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int* lengths,
                               void* out, float* lse, void* ws, const Dims& dm, int window,
