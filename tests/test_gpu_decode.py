@@ -52,6 +52,14 @@ CASES += [("bf16", 64, 2, 24, 2, 700, [700, 1], -1, "bhtd")]  # 12 query heads p
 CASES += [("bf16", 128, 2, 8, 2, 40000, [40000, 12345], -1, "bhtd"),
           ("bf16", 64, 1, 8, 8, 100000, [99999], 70000, "bthd"),
           ("f32", 128, 1, 4, 2, 70000, None, -1, "bhtd")]
+# Many (batch, kv head) pairs and short caches: one split per pair, written without the merge
+# (at d = 64 up to 1024 keys; the next size takes the split path).
+CASES += [("bf16", 64, 16, 8, 8, 1024, [1024, 1, 513, 1000] * 4, -1, "bhtd"),
+          ("bf16", 64, 16, 8, 8, 1025, None, -1, "bhtd"),
+          ("bf16", 64, 16, 8, 8, 1100, [1100, 7] * 8, 300, "bthd"),
+          ("bf16", 128, 32, 8, 4, 512, None, 100, "bthd"),
+          ("bf16", 32, 8, 16, 16, 2048, [2048, 2, 1500, 999] * 2, -1, "bhtd"),
+          ("f32", 16, 4, 32, 32, 700, [700, 1, 350, 699], 64, "bhtd")]
 
 
 @pytest.mark.parametrize("dt,d,B,H,H_kv,S,lengths,window,layout", CASES,

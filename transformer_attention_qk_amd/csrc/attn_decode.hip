@@ -12,9 +12,10 @@
 // bf16, every load issued before the first use) and, for every query head of the group (GQA: the
 // cache is read once for the whole group), forms the scores (fp32), their maximum m, the weights
 // exp2(s - m), their sum l and the weighted sum of the V rows with shuffles inside the wave only.
-// The four waves' (m, l, o) meet in LDS, one barrier per query head, and the workgroup writes its
-// split's o, unnormalised, with m and l to the caller's workspace. A merge kernel combines the
-// splits of each (batch, head):
+// The four waves' (m, l, o) meet in LDS, one barrier per query head. With one split per
+// (batch, kv head) (many heads, short caches) the workgroup writes out and lse itself; otherwise
+// it writes its split's o, unnormalised, with m and l to the caller's workspace, and a merge
+// kernel combines the splits of each (batch, head):
 //   M = max_c m_c,  L = sum_c l_c 2^(m_c - M),  out = sum_c o_c 2^(m_c - M) / L,
 //   lse = (M + log2 L) ln 2.
 // The weights stay fp32 (no bf16 rounding), every sum is fp32, out is rounded once.
@@ -34,6 +35,10 @@ constexpr int kDecodeWaves = 4;  // waves per workgroup, each with its own rows
 constexpr int decode_wave_keys(int d) { return d >= 4096 ? 1 : 4096 / d; }
 constexpr int decode_split_keys(int d) { return kDecodeWaves * decode_wave_keys(d); }
 constexpr int kDecodeTargetGroups = 2048;
+// One split per (batch, kv head) instead, written out without a merge, when those workgroups give
+// at least kDecodeSingleWaves waves and each wave takes at most kDecodeSingleBatches batches.
+constexpr int kDecodeSingleWaves = 512;
+constexpr int kDecodeSingleBatches = 4;
 
 template <typename Elem, int D>
 struct DecCfg {
@@ -65,11 +70,14 @@ __device__ __forceinline__ void chunk_f32(u32x4 w, float (&x)[16 / sizeof(Elem)]
   }
 }
 
-template <typename Elem, int D>
+// FINAL: one split per (batch, kv head) (n_split = 1); the workgroup writes out and lse itself
+// and the workspace is not touched.
+template <typename Elem, int D, bool FINAL>
 __global__ __launch_bounds__(256) void attn_decode_partial(
     const Elem* __restrict__ Qv, const Elem* __restrict__ K, const Elem* __restrict__ V,
-    const int* __restrict__ lengths, float* __restrict__ ws, Geometry geo, int H_kv, int S,
-    int window, int n_split, int64_t parts, float scale_log2) {
+    const int* __restrict__ lengths, float* __restrict__ ws, Elem* __restrict__ out,
+    float* __restrict__ lse, Geometry geo, int H_kv, int S, int window, int n_split,
+    int64_t parts, float scale_log2) {
   using C = DecCfg<Elem, D>;
   // Per query head (two heads alternate, so one barrier per head suffices): each wave's
   // unnormalised o[D], then its m and l.
@@ -198,11 +206,16 @@ __global__ __launch_bounds__(256) void attn_decode_partial(
           o = fmaf(rp[w][tid], fw, o);
         }
       }
-      const int64_t part = ((int64_t)b * H + h) * n_split + split;
-      ws_o[part * D + tid] = o;
-      if (tid == 0) {
-        ws_m[part] = M;
-        ws_l[part] = L;
+      if constexpr (FINAL) {  // L > 0: the entry has a key, and it is in this split
+        out[((int64_t)b * H + h) * D + tid] = (Elem)(o * (1.0f / L));
+        if (tid == 0 && lse != nullptr) lse[(int64_t)b * H + h] = (M + __log2f(L)) * kLn2;
+      } else {
+        const int64_t part = ((int64_t)b * H + h) * n_split + split;
+        ws_o[part * D + tid] = o;
+        if (tid == 0) {
+          ws_m[part] = M;
+          ws_l[part] = L;
+        }
       }
     }
   }
@@ -275,13 +288,25 @@ template <typename Elem, int D>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const int* lengths,
                                   void* out, float* lse, void* ws, const Dims& dm, int window,
                                   hipStream_t stream) {
-  const int n_split = decode_splits(dm.B, dm.H, dm.T, D, window);
-  const int64_t parts = (int64_t)dm.B * dm.H * n_split;
   const Geometry geo = make_geometry(dm);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-  hipLaunchKernelGGL((attn_decode_partial<Elem, D>), dim3((unsigned)(dm.B * dm.H_kv * n_split)),
-                     dim3(256), 0, stream, (const Elem*)q, (const Elem*)k, (const Elem*)v, lengths,
-                     (float*)ws, geo, dm.H_kv, dm.T, window, n_split, parts, scale_log2);
+  // One split per (batch, kv head), with no merge launch, when those workgroups alone give
+  // kDecodeSingleWaves waves and no wave takes more than kDecodeSingleBatches batches.
+  const int keys = (window >= 0 && window + 1 < dm.T) ? window + 1 : dm.T;
+  if ((int64_t)dm.B * dm.H_kv * kDecodeWaves >= kDecodeSingleWaves &&
+      keys <= kDecodeSingleBatches * decode_split_keys(D)) {
+    hipLaunchKernelGGL((attn_decode_partial<Elem, D, true>), dim3((unsigned)(dm.B * dm.H_kv)),
+                       dim3(256), 0, stream, (const Elem*)q, (const Elem*)k, (const Elem*)v,
+                       lengths, (float*)ws, (Elem*)out, lse, geo, dm.H_kv, dm.T, window, 1,
+                       (int64_t)dm.B * dm.H, scale_log2);
+    return hipGetLastError();
+  }
+  const int n_split = decode_splits(dm.B, dm.H, dm.T, D, window);
+  const int64_t parts = (int64_t)dm.B * dm.H * n_split;
+  hipLaunchKernelGGL((attn_decode_partial<Elem, D, false>),
+                     dim3((unsigned)(dm.B * dm.H_kv * n_split)), dim3(256), 0, stream,
+                     (const Elem*)q, (const Elem*)k, (const Elem*)v, lengths, (float*)ws,
+                     (Elem*)out, lse, geo, dm.H_kv, dm.T, window, n_split, parts, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_merge<Elem, D>), dim3((unsigned)(dm.B * dm.H)), dim3(256), 0,
