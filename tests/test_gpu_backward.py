@@ -205,6 +205,29 @@ def test_bwd_outputs_stay_inside_their_buffers():
         assert bool((big[:pad] == 3.0).all()) and bool((big[-pad:] == 3.0).all())
 
 
+@pytest.mark.parametrize("dt,d,layout", [("bf16", 64, "bthd"), ("bf16", 128, "bhtd"),
+                                          ("bf16", 32, "bhtd"), ("f32", 16, "bthd")])
+def test_bwd_delta_by_product(dt, d, layout):
+    """delta (written by the dQ kernel in bf16, by its own kernel in fp32) is rowsum(dout * out)
+    of the exact values handed over, within fp32 summation rounding; ragged T = 150."""
+    B, H, H_kv, T = 2, 4, 2, 150
+    say(f"bwd delta {dt} d={d} {layout}")
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    shp = lambda h: (B, T, h, d) if layout == "bthd" else (B, h, T, d)
+    q, do = (inputs.make_random(shp(H), dtype, s).cuda() for s in (471, 474))
+    k, v = (inputs.make_random(shp(H_kv), dtype, s).cuda() for s in (472, 473))
+    out, lse = ops.attn_fwd(q, k, v, window=40, layout=layout)
+    delta = torch.full((B, H, T), 7.0, dtype=torch.float32, device="cuda")
+    ops.attn_bwd(q, k, v, out, lse, do, window=40, delta=delta, layout=layout)
+    torch.cuda.synchronize()
+    ref = np.sum(f64(out) * f64(do), axis=-1)  # [B, T, H] or [B, H, T]
+    if layout == "bthd":
+        ref = ref.transpose(0, 2, 1)
+    err = np.abs(f64(delta) - ref) / np.maximum(1.0, np.abs(ref))
+    say(f"   max rel err {float(err.max()):.2e}")
+    assert float(err.max()) <= 1e-5
+
+
 def test_bwd_full_size_sampled():
     """The headline shape's first two layers (windows 512 and, as the last layer, 1024) at full
     size (B=16, H=12, T=1024, d=64); the oracle checks sampled heads in full."""

@@ -11,8 +11,13 @@
 //   dQ_i = c sum_j dS_ij k_j          dK_j = c sum_i dS_ij q_i
 // Grouped-query heads: a kv head's dK, dV sum over the query heads of its group.
 //
-// Three kernels per call:
-//   - attn_bwd_delta: D_i = dO_i . O_i in fp32 (HBM bound, one pass over out and dout).
+// Kernels per bf16 call, in launch order:
+//   - attn_bwd_dq_bf16: one workgroup per (batch * head, block of 128 queries), wave w owning
+//     queries [32 w, 32 w + 32): the forward's layout (S^T = K Q^T, lane = query), with
+//     dP^T = V dO^T beside it and dQ^T += K^T dS^T. It also forms D_i = dO_i . O_i in fp32 for
+//     its rows (their dO is in registers already, so D_i costs one read of the row's O) and
+//     writes it for the next kernel. The fp32 path runs attn_bwd_delta (one pass over out and
+//     dout) for D instead.
 //   - attn_bwd_dkdv_bf16: one workgroup per (batch, kv head, block of 128 keys), wave w owning
 //     keys [32 w, 32 w + 32). The wave keeps its K and V rows in registers (B operands) and
 //     walks the query tiles that see its keys (all query heads of the group), staged in LDS:
@@ -20,9 +25,6 @@
 //     accumulators each lane owns one key and 16 queries, so P and dS are formed in place and
 //     feed dV^T += dO^T P and dK^T += Q^T dS as B operands, with A = dO^T, Q^T read from the
 //     same tiles by transposing LDS reads (ds_read_b64_tr_b16).
-//   - attn_bwd_dq_bf16: one workgroup per (batch * head, block of 128 queries), wave w owning
-//     queries [32 w, 32 w + 32): the forward's layout (S^T = K Q^T, lane = query), with
-//     dP^T = V dO^T beside it and dQ^T += K^T dS^T.
 // Computing dQ in its own kernel recomputes S and dP once more instead of accumulating dQ across
 // key blocks with atomics: no scratch memory and no ordering nondeterminism.
 // P and dS are rounded to bf16 (nearest even) for the matrix products; every accumulation is
@@ -412,9 +414,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16(
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    bf16* __restrict__ dQ, Geometry geo, int BH, int T, int window_arg, float scale_log2,
-    float scale, int nqb, int group_heads) {
+    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ Delta, bf16* __restrict__ dQ, Geometry geo, int BH, int T,
+    int window_arg, float scale_log2, float scale, int nqb, int group_heads) {
   using C = BwdCfg<D>;
   // Two buffers, each: K tile, V tile.
   constexpr int BUF = 2 * C::TILE_BYTES;
@@ -441,7 +443,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16(
     dof[s] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, off));
   }
   const float lse2 = (qi < T) ? LSE[(int64_t)bh * T + qi] * kLog2e : 0.f;
-  const float dlt = (qi < T) ? Delta[(int64_t)bh * T + qi] : 0.f;
+  // D_i = dO_i . O_i (fp32) from the lane's half of the row and its partner's (lane ^ 32), with
+  // O read in dO's pattern; written for the dK/dV kernel, which runs after this one. Rows past T
+  // read as zero and are not written.
+  float dlt;
+  {
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc(O + qoff, T * q_rs);
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const u32x4 ow = buffer_load16(ro, (uint32_t)(qi * q_rs + 32 * s + 16 * hi));
+      const u32x4 dw = __builtin_bit_cast(u32x4, dof[s]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = fmaf(bf16lo_to_f32(dw[e]), bf16lo_to_f32(ow[e]), part);
+        part = fmaf(bf16hi_to_f32(dw[e]), bf16hi_to_f32(ow[e]), part);
+      }
+    }
+    dlt = part + __shfl_xor(part, 32);
+    if (qi < T && hi == 0) Delta[(int64_t)bh * T + qi] = dlt;
+  }
   f32x16 dqa[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
@@ -641,10 +662,12 @@ static hipError_t launch_delta_t(const void* out, const void* dout, float* delta
   return hipGetLastError();
 }
 
+// dQ first: its kernel also forms delta, which the dK/dV kernel reads.
 template <int D, int MODE>
-static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dout,
-                                    const float* lse, const float* delta, void* dq, void* dk,
-                                    void* dv, const Dims& dm, int window, hipStream_t stream) {
+static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* out,
+                                    const void* dout, const float* lse, float* delta, void* dq,
+                                    void* dk, void* dv, const Dims& dm, int window,
+                                    hipStream_t stream) {
   const Geometry geo = make_geometry(dm);
   const float scale = (float)(1.0 / sqrt((double)D));
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -659,20 +682,20 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
                        nkb, gh);
     return hipGetLastError();
   };
-  hipError_t e;
+  const int BH = dm.B * dm.H;
+  hipLaunchKernelGGL((attn_bwd_dq_bf16<D, MODE>), dim3((unsigned)(BH * nkb)), dim3(256), 0,
+                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)out,
+                     (const bf16*)dout, lse, delta, (bf16*)dq, geo, BH, dm.T, window, scale_log2,
+                     scale, nkb, group_heads(BH, (int64_t)dm.T * D * 2 * 2));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if constexpr (D <= 64) {
     e = dkdv(std::integral_constant<int, kBothPasses>{});
   } else {
     e = dkdv(std::integral_constant<int, kPassDV>{});
     if (e == hipSuccess) e = dkdv(std::integral_constant<int, kPassDK>{});
   }
-  if (e != hipSuccess) return e;
-  const int BH = dm.B * dm.H;
-  hipLaunchKernelGGL((attn_bwd_dq_bf16<D, MODE>), dim3((unsigned)(BH * nkb)), dim3(256), 0,
-                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                     lse, delta, (bf16*)dq, geo, BH, dm.T, window, scale_log2, scale, nkb,
-                     group_heads(BH, (int64_t)dm.T * D * 2 * 2));
-  return hipGetLastError();
+  return e;
 }
 
 template <int D, int MODE>
@@ -702,13 +725,11 @@ static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, cons
   if constexpr (D < 32) {
     if (dtype == 0) return hipErrorInvalidValue;  // bf16 needs d >= 32 (32-wide MFMA tiles)
   }
-  hipError_t e;
-  if constexpr (D >= 32)
-    e = (dtype == 0) ? launch_delta_t<bf16, D>(out, dout, delta, dm, stream)
-                     : launch_delta_t<float, D>(out, dout, delta, dm, stream);
-  else
-    e = launch_delta_t<float, D>(out, dout, delta, dm, stream);
-  if (e != hipSuccess) return e;
+  // bf16: the dQ kernel forms delta itself; fp32: the delta kernel runs first.
+  if (dtype != 0) {
+    const hipError_t e = launch_delta_t<float, D>(out, dout, delta, dm, stream);
+    if (e != hipSuccess) return e;
+  }
   // A window of T - 1 or more hides nothing: run it as plain causal (as the forward does).
   const int mode = !causal ? kNonCausal
                            : ((window >= 0 && window < dm.T - 1) ? kCausalWindow : kCausal);
@@ -716,7 +737,8 @@ static hipError_t launch_bwd_d(const void* q, const void* k, const void* v, cons
   if (mode == M) {                                                                              \
     if constexpr (D >= 32) {                                                                    \
       if (dtype == 0)                                                                           \
-        return launch_bwd_bf16_t<D, M>(q, k, v, dout, lse, delta, dq, dk, dv, dm, window, stream); \
+        return launch_bwd_bf16_t<D, M>(q, k, v, out, dout, lse, delta, dq, dk, dv, dm, window,  \
+                                       stream);                                                 \
     }                                                                                           \
     return launch_bwd_f32_t<D, M>(q, k, v, dout, lse, delta, dq, dk, dv, dm, window, stream);   \
   }
