@@ -37,7 +37,7 @@ constexpr int decode_split_keys(int d) { return kDecodeWaves * decode_wave_keys(
 constexpr int kDecodeTargetGroups = 2048;
 // One split per (batch, kv head) instead, written out without a merge, when those workgroups give
 // at least kDecodeSingleWaves waves and each wave takes at most kDecodeSingleBatches batches.
-constexpr int kDecodeSingleWaves = 512;
+constexpr int kDecodeSingleWaves = 256;
 constexpr int kDecodeSingleBatches = 4;
 
 template <typename Elem, int D>
