@@ -328,7 +328,8 @@ int attn_value_gate_bwd_ex(const void* ve, const void* gate_logits, const void* 
  *   lengths          DEVICE int32 [B]: n_b, clamped to [1, S] on the device; NULL: every n_b = S
  *   lse              DEVICE fp32 [B][H], written; may be NULL
  *   workspace        DEVICE scratch of at least attn_decode_workspace_bytes(B, H, S, d, window)
- *                    bytes (16-byte aligned), owned by the caller; contents are overwritten and
+ *                    bytes (16-byte aligned), owned by the caller; its contents may be
+ *                    overwritten (shapes with one key split per head leave it untouched) and
  *                    calls that share one workspace must be ordered on one stream
  *   window           -1 or >= 0 (else ATTN_ERR_WINDOW)
  *   d, dtype         ATTN_BF16: {32, 64, 128}; ATTN_F32: {16, 32, 64, 128}
