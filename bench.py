@@ -29,7 +29,9 @@ T=2048, d=128, eight layers "SSSL" with windows 1024 / 2048) on q, k, v in the p
 bf16 configurations (andrea12m, andrea480m_sssl, long_sssl) run the same way in [B][H][T][d].
 
 Extra modes (used to collect rocprofv3 counters; they print no JSON):
-  --only attn|kprologue|attn_unfused|prologue   run only that kernel, --steps times per layer
+  --only attn|kprologue|attn_unfused|prologue|decode
+                         run only that kernel (decode: its two kernels, or one where a
+                         single key split per head suffices), --steps times per layer
   --copy-calibration     run a plain 256 MiB device copy (known bytes) for counter scaling
 """
 
@@ -157,7 +159,7 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward, decode and value-gate timings")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
-    ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue"],
+    ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue", "decode"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -268,15 +270,36 @@ def main() -> int:
         return lib.attn_fwd_ex(pqn, pkn, pv, po, pl, B, H, H, T, d, lay, windows[l], 1, bf16,
                                stream)
 
+    def make_decode():
+        """Decode inputs: each layer's newest normalised query (from qn, so the two-call prologue
+        must have run) against its normalised keys and values as a full cache of T tokens."""
+        qdec = [qn[l][:, :, -1].contiguous() if layout == "bhtd" else qn[l][:, -1].contiguous()
+                for l in range(L)]
+        dout_dec = [torch.empty_like(x) for x in qdec]
+        dlse_dec = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(L)]
+        wsb = [lib.attn_decode_workspace_bytes(B, H, T, d, windows[l]) for l in range(L)]
+        ws_dec = [torch.empty((n // 4 + 4,), dtype=torch.float32, device="cuda") for n in wsb]
+        PD = [tuple(t.data_ptr() for t in (qdec[l], dout_dec[l], dlse_dec[l], ws_dec[l]))
+              for l in range(L)]
+
+        def decode_step(l):
+            _, _, pv, _, pkn, _, _ = P[l]
+            pqd, pod, pld, pws = PD[l]
+            return lib.attn_decode_ex(pqd, pkn, pv, None, pod, pld, pws, wsb[l], B, H, H, T, d,
+                                      lay, windows[l], bf16, stream)
+        decode_step.buffers = (qdec, dout_dec, dlse_dec, ws_dec)  # alive while it is
+        return decode_step, wsb
+
     if args.only:
         # inputs of the chosen kernel only, so a counter run sees no other kernel of its kind
-        setup = {"attn": kprologue, "attn_unfused": prologue}.get(args.only)
+        setup = {"attn": kprologue, "attn_unfused": prologue, "decode": prologue}.get(args.only)
         if setup is not None:
             for l in range(L):
                 setup(l)
         torch.cuda.synchronize()
         fn = {"attn": attention, "kprologue": kprologue, "attn_unfused": attention_unfused,
-              "prologue": prologue}[args.only]
+              "prologue": prologue,
+              "decode": make_decode()[0] if args.only == "decode" else None}[args.only]
         for _ in range(args.steps):
             for l in range(L):
                 _lib.check(args.only, fn(l))
@@ -379,20 +402,7 @@ def main() -> int:
     # Decode (context): one generation step against each layer's keys and values as the cache.
     dec_ms = None
     if not args.no_backward:
-        qdec = [qn[l][:, :, -1].contiguous() if layout == "bhtd" else qn[l][:, -1].contiguous()
-                for l in range(L)]
-        dout_dec = [torch.empty_like(x) for x in qdec]
-        dlse_dec = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in range(L)]
-        wsb = [lib.attn_decode_workspace_bytes(B, H, T, d, windows[l]) for l in range(L)]
-        ws_dec = [torch.empty((n // 4 + 4,), dtype=torch.float32, device="cuda") for n in wsb]
-        PD = [tuple(t.data_ptr() for t in (qdec[l], dout_dec[l], dlse_dec[l], ws_dec[l]))
-              for l in range(L)]
-
-        def decode_step(l):
-            _, _, pv, _, pkn, _, _ = P[l]
-            pqd, pod, pld, pws = PD[l]
-            return lib.attn_decode_ex(pqd, pkn, pv, None, pod, pld, pws, wsb[l], B, H, H, T, d,
-                                      lay, windows[l], bf16, stream)
+        decode_step, _ = make_decode()
 
         def nothing(l):
             return 0
@@ -403,8 +413,8 @@ def main() -> int:
         dec_bytes = [B * H * (min(T, W + 1 if W >= 0 else T) * 4 * d + 4 * d) for W in windows]
 
     # The backward pass (context, not the value): per layer, the gradient of sum(dout * out)
-    # through attn_bwd_ex on the normalised q, k the two-call path wrote (kernels: delta, dK/dV,
-    # dQ), then the prologue's backward attn_qknorm_rope_bwd_ex in place.
+    # through attn_bwd_ex on the normalised q, k the two-call path wrote (kernels: dQ, which also
+    # forms delta, then dK/dV), then the prologue's backward attn_qknorm_rope_bwd_ex in place.
     bwd_ms = None
     if not args.no_backward:
         dout, dq, dk, dv, delta = ([] for _ in range(5))
