@@ -166,9 +166,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the attention path runs on a single MI355X and this "
-              "build has no multi-GPU mode (the sharding plan is described in DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the attention path runs on a single MI355X and has no "
+              "multi-GPU mode (its (batch, head) work items are independent, so a batch shards "
+              "across GPUs without communication). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch

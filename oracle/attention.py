@@ -20,7 +20,7 @@ Sources (page title, then the part of the page used):
 [CNOYU] The web3.cnoyu.net commentary on autoresearch's train.py: the passage on QK-norm and on
         the SSSL window pattern.
 
-Readings taken where the pages are silent or disagree (each also listed in the design doc):
+Readings taken where the pages are silent or disagree:
 
 R1  RMSNorm has no weight and eps = 1e-6 ([HABR] ``norm`` passes no eps or weight).
 R2  Norm then RoPE. [HABR] ``CausalSelfAttention.forward`` rotates first and normalises second.
