@@ -29,9 +29,10 @@ T=2048, d=128, eight layers "SSSL" with windows 1024 / 2048) on q, k, v in the p
 bf16 configurations (andrea12m, andrea480m_sssl, long_sssl) run the same way in [B][H][T][d].
 
 Extra modes (used to collect rocprofv3 counters; they print no JSON):
-  --only attn|kprologue|attn_unfused|prologue|decode
+  --only attn|kprologue|attn_unfused|prologue|decode|bwd
                          run only that kernel (decode: its two kernels, or one where a
-                         single key split per head suffices), --steps times per layer
+                         single key split per head suffices; bwd: attn_bwd_ex's kernels, after
+                         the two-call forward it reads), --steps times per layer
   --copy-calibration     run a plain 256 MiB device copy (known bytes) for counter scaling
 """
 
@@ -159,8 +160,8 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward, decode and value-gate timings")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
-    ap.add_argument("--only", choices=["attn", "kprologue", "attn_unfused", "prologue", "decode"],
-                    default=None)
+    ap.add_argument("--only", default=None,
+                    choices=["attn", "kprologue", "attn_unfused", "prologue", "decode", "bwd"])
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -290,6 +291,37 @@ def main() -> int:
         decode_step.buffers = (qdec, dout_dec, dlse_dec, ws_dec)  # alive while it is
         return decode_step, wsb
 
+    def make_backward():
+        """Backward inputs: dout per layer and gradient buffers; runs the two-call forward (q, k
+        normalised into qn, kn, then out and lse) whose saved tensors the backward reads."""
+        dout, dq, dk, dv, delta = ([] for _ in range(5))
+        for l in range(L):
+            dout.append(inputs.make_random(tuple(q[l].shape), torch.bfloat16, 900 + l).cuda())
+            dq.append(torch.empty_like(q[l]))
+            dk.append(torch.empty_like(k[l]))
+            dv.append(torch.empty_like(v[l]))
+            delta.append(torch.empty_like(lse[l]))
+        for l in range(L):
+            _lib.check("prologue", prologue(l))
+            _lib.check("attn_unfused", attention_unfused(l))
+        torch.cuda.synchronize()
+        PB = [tuple(t.data_ptr() for t in (dout[l], dq[l], dk[l], dv[l], delta[l]))
+              for l in range(L)]
+
+        def attention_bwd(l):
+            _, _, pv, pqn, pkn, po, pl = P[l]
+            pdo, pdq, pdk, pdv, pdl = PB[l]
+            return lib.attn_bwd_ex(pqn, pkn, pv, po, pdo, pl, pdl, pdq, pdk, pdv, B, H, H, T, d,
+                                   lay, windows[l], 1, bf16, stream)
+
+        def prologue_bwd(l):
+            pq, pk, _, _, _, _, _ = P[l]
+            _, pdq, pdk, _, _ = PB[l]
+            return lib.attn_qknorm_rope_bwd_ex(pq, pk, pdq, pdk, pdq, pdk, pcos, psin, B, H, H, T,
+                                               d, lay, eps, bf16, stream)
+        attention_bwd.buffers = (dout, dq, dk, dv, delta)  # alive while it is
+        return attention_bwd, prologue_bwd
+
     if args.only:
         # inputs of the chosen kernel only, so a counter run sees no other kernel of its kind
         setup = {"attn": kprologue, "attn_unfused": prologue, "decode": prologue}.get(args.only)
@@ -299,7 +331,8 @@ def main() -> int:
         torch.cuda.synchronize()
         fn = {"attn": attention, "kprologue": kprologue, "attn_unfused": attention_unfused,
               "prologue": prologue,
-              "decode": make_decode()[0] if args.only == "decode" else None}[args.only]
+              "decode": make_decode()[0] if args.only == "decode" else None,
+              "bwd": make_backward()[0] if args.only == "bwd" else None}[args.only]
         for _ in range(args.steps):
             for l in range(L):
                 _lib.check(args.only, fn(l))
@@ -417,32 +450,7 @@ def main() -> int:
     # forms delta, then dK/dV), then the prologue's backward attn_qknorm_rope_bwd_ex in place.
     bwd_ms = None
     if not args.no_backward:
-        dout, dq, dk, dv, delta = ([] for _ in range(5))
-        for l in range(L):
-            dout.append(inputs.make_random(tuple(q[l].shape), torch.bfloat16, 900 + l).cuda())
-            dq.append(torch.empty_like(q[l]))
-            dk.append(torch.empty_like(k[l]))
-            dv.append(torch.empty_like(v[l]))
-            delta.append(torch.empty_like(lse[l]))
-        for l in range(L):
-            _lib.check("prologue", prologue(l))
-            _lib.check("attn_unfused", attention_unfused(l))
-        torch.cuda.synchronize()
-        PB = [tuple(t.data_ptr() for t in (dout[l], dq[l], dk[l], dv[l], delta[l]))
-              for l in range(L)]
-
-        def attention_bwd(l):
-            _, _, pv, pqn, pkn, po, pl = P[l]
-            pdo, pdq, pdk, pdv, pdl = PB[l]
-            return lib.attn_bwd_ex(pqn, pkn, pv, po, pdo, pl, pdl, pdq, pdk, pdv, B, H, H, T, d,
-                                   lay, windows[l], 1, bf16, stream)
-
-        def prologue_bwd(l):
-            pq, pk, _, _, _, _, _ = P[l]
-            _, pdq, pdk, _, _ = PB[l]
-            return lib.attn_qknorm_rope_bwd_ex(pq, pk, pdq, pdk, pdq, pdk, pcos, psin, B, H, H, T,
-                                               d, lay, eps, bf16, stream)
-
+        attention_bwd, prologue_bwd = make_backward()
         for l in range(L):
             _lib.check("attn_bwd", attention_bwd(l))
             _lib.check("prologue_bwd", prologue_bwd(l))
