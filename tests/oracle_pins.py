@@ -149,6 +149,78 @@ def check_sdpa_special_case(o, seed=1):
                                    err_msg=f"W={window} causal={causal}")
 
 
+def _sdpa_reference(q, k, v, window, causal):
+    """PyTorch CPU scaled_dot_product_attention in fp64 with an explicit boolean mask built from
+    the window reading (key j visible to query i iff j <= i and i - j <= W); kv heads are
+    repeated for their query group. Returns (out, lse) as numpy arrays; the logsumexp is
+    torch.logsumexp of the masked scaled scores."""
+    import torch
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)) for x in (q, k, v))
+    T, d = q.shape[-2], q.shape[-1]
+    g = q.shape[1] // k.shape[1]
+    k = k.repeat_interleave(g, dim=1)
+    v = v.repeat_interleave(g, dim=1)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    mask = torch.ones(T, T, dtype=torch.bool)
+    if causal:
+        mask = j <= i
+        if window >= 0:
+            mask = mask & (i - j <= window)
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    s = (q @ k.transpose(-1, -2)) / math.sqrt(d)
+    lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)
+    return out.numpy(), lse.numpy()
+
+
+def check_blocked_rows(o, seed=18):
+    """The oracle's row blocks and its sampled-row path against whole-matrix references.
+
+    At T = 600 the default block of 256 rows gives three blocks, so the key range of a block
+    that starts past the window (lo = r0 - W > 0) is exercised at every window around the block
+    size, including the inclusive boundary key r0 - W (the window reading of the (W, 0) call in
+    the train.py listing's ``CausalSelfAttention.forward``; "A Máscara Causal"). The reference
+    is torch's fp64 ``scaled_dot_product_attention`` with an explicit mask over all T keys.
+    Then ``rows=`` with unsorted, repeated and non-contiguous query indices that straddle block
+    boundaries (tiny blocks of 7 rows, grouped kv heads) must equal the matching rows of the
+    full result, and the same through ``attention_layer``."""
+    rng = _rng(seed)
+    B, H, H_kv, T, d = 1, 2, 1, 600, 8
+    q = rng.standard_normal((B, H, T, d)) * 1.5
+    k = rng.standard_normal((B, H_kv, T, d)) * 1.5
+    v = rng.standard_normal((B, H_kv, T, d + 3))
+    for window in (-1, 0, 1, 255, 256, 257, 343, 511, 599):
+        ref_o, ref_l = _sdpa_reference(q, k, v, window, True)
+        out, lse = o.attention(q, k, v, window=window, causal=True)
+        np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12, err_msg=f"W={window}")
+        np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12, err_msg=f"W={window}")
+    # Sampled rows: block boundaries of 256 and of 7, unsorted, with a repeat.
+    rows = np.array([599, 0, 256, 255, 7, 6, 511, 512, 300, 13, 14, 257, 0, 598])
+    Ts = 40
+    qs, ks, vs = q[:, :, :Ts], k[:, :, :Ts], v[:, :, :Ts]
+    rows_s = np.array([39, 0, 7, 6, 13, 14, 21, 3, 35, 20, 7])
+    for window, causal in ((-1, True), (0, True), (3, True), (6, True), (7, True), (38, True),
+                           (-1, False)):
+        full_o, full_l = o.attention(qs, ks, vs, window=window, causal=causal)
+        for blk in (1, 7, 256):
+            out, lse = o.attention(qs, ks, vs, window=window, causal=causal, rows=rows_s, block=blk)
+            np.testing.assert_allclose(out, full_o[:, :, rows_s], rtol=0, atol=1e-13,
+                                       err_msg=f"W={window} causal={causal} block={blk}")
+            np.testing.assert_allclose(lse, full_l[:, :, rows_s], rtol=0, atol=1e-13)
+        ref_o, ref_l = _sdpa_reference(qs, ks, vs, window, causal)
+        np.testing.assert_allclose(full_o, ref_o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(full_l, ref_l, rtol=0, atol=1e-12)
+    for window in (-1, 256, 300):
+        ref_o, ref_l = _sdpa_reference(q, k, v, window, True)
+        out, lse = o.attention(q, k, v, window=window, causal=True, rows=rows)
+        np.testing.assert_allclose(out, ref_o[:, :, rows], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_l[:, :, rows], rtol=0, atol=1e-12)
+        lo, ll = o.attention_layer(q, k, v, window=window, rows=rows)
+        fo, fl = o.attention_layer(q, k, v, window=window)
+        np.testing.assert_allclose(lo, fo[:, :, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(ll, fl[:, :, rows], rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------------------------
 # Invariants of the definition.
 # ---------------------------------------------------------------------------------------------
@@ -448,6 +520,32 @@ def check_backward_torch_autograd(o, seed=13):
                 assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-11), (window, causal, layer)
 
 
+def check_backward_blocked(o, seed=19):
+    """The backward's row blocks (three blocks of 256 rows at T = 600, windows around the block
+    size and the inclusive boundary key r0 - W) against fp64 autograd of torch's
+    ``scaled_dot_product_attention`` with an explicit mask over all T keys, grouped kv heads."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(seed)
+    B, H, H_kv, T, d = 1, 2, 1, 600, 8
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    for window in (-1, 0, 255, 256, 257, 511):
+        arrs = [rng.standard_normal(s) for s in ((B, H, T, d), (B, H_kv, T, d), (B, H_kv, T, d),
+                                                (B, H, T, d))]
+        q, k, v, do = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in arrs)
+        mask = j <= i
+        if window >= 0:
+            mask = mask & (i - j <= window)
+        out = F.scaled_dot_product_attention(q, k.repeat_interleave(H // H_kv, dim=1),
+                                             v.repeat_interleave(H // H_kv, dim=1), attn_mask=mask)
+        gq, gk, gv = torch.autograd.grad((out * do.detach()).sum(), (q, k, v))
+        dq, dk, dv = o.attention_backward(*arrs, window=window, causal=True)
+        for mine, ref in ((dq, gq), (dk, gk), (dv, gv)):
+            assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-11), window
+
+
 def check_backward_invariants(o, seed=14):
     """Exact properties of the gradients: every row of dS sums to zero, so the keys' gradients
     of a head sum to zero; with window 0 each query sees only its own key, so dq = dk = 0 and
@@ -613,6 +711,7 @@ BACKWARD_CHECKS = [
     check_backward_finite_differences,
     check_layer_backward_finite_differences,
     check_backward_torch_autograd,
+    check_backward_blocked,
     check_backward_invariants,
 ]
 
@@ -622,6 +721,7 @@ ALL_CHECKS = [
     check_worked_example_qknorm,
     check_brute_force,
     check_sdpa_special_case,
+    check_blocked_rows,
     check_weights_sum_to_one,
     check_masked_entries_have_no_weight,
     check_window_T_is_causal,

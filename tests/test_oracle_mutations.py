@@ -304,3 +304,44 @@ def test_unmutated_gate_copy_passes():
 @pytest.mark.parametrize("name", list(GATE_MUTANTS))
 def test_gate_mutations_are_caught(name):
     assert _fails(_gate_mutant(**GATE_MUTANTS[name]), pins.VALUE_GATE_CHECKS), name
+
+
+# Row blocks and sampled rows: the key range of a block that starts past the window, and the
+# order of sampled rows.
+def _key_range_drops_boundary(r0, r1, T, window, causal):
+    """Key range one short at the window's inclusive boundary key r0 - W of a later block."""
+    if not causal:
+        return 0, T
+    return (0 if window < 0 else max(0, r0 - window + 1)), min(T, r1)
+
+
+def _key_range_one_past(r0, r1, T, window, causal):
+    """Key range that ends one key early (the block's last row loses its own key)."""
+    if not causal:
+        return 0, T
+    return (0 if window < 0 else max(0, r0 - window)), min(T, r1 - 1)
+
+
+@pytest.mark.parametrize("name,fn", [("window boundary key dropped", _key_range_drops_boundary),
+                                     ("block's last key dropped", _key_range_one_past)])
+def test_key_range_mutations_are_caught(name, fn, monkeypatch):
+    import sys
+    monkeypatch.setattr(sys.modules["oracle.attention"], "_key_range", fn)
+    monkeypatch.setattr(sys.modules["oracle.backward"], "_key_range", fn)
+    assert _fails(oracle, [pins.check_blocked_rows]), name
+    assert _fails(oracle, [pins.check_backward_blocked]), name
+
+
+def _attention_sorted_rows(q, k, v, window=-1, causal=True, rows=None, block=256):
+    """Sampled rows returned in sorted order instead of the order asked for."""
+    if rows is not None:
+        rows = np.sort(np.asarray(rows))
+    return oracle.attention(q, k, v, window, causal, rows=rows, block=block)
+
+
+def test_sampled_row_order_mutation_is_caught():
+    assert _fails(_mutant(attention=_attention_sorted_rows), [pins.check_blocked_rows])
+
+
+def test_key_range_unmutated_passes():
+    assert not _fails(oracle, [pins.check_blocked_rows, pins.check_backward_blocked])
