@@ -704,13 +704,16 @@ static hipError_t launch_bwd_f32_t(const void* q, const void* k, const void* v, 
                                    void* dv, const Dims& dm, int window, hipStream_t stream) {
   const Geometry geo = make_geometry(dm);
   const float scale = (float)(1.0 / sqrt((double)D));
+  // Thread counts fit in int (checked by the entry point); the grids are formed in 64 bits so
+  // that rounding up to whole workgroups cannot overflow.
   const int nq = dm.B * dm.H * dm.T * (D / 16), nk = dm.B * dm.H_kv * dm.T * (D / 16);
-  hipLaunchKernelGGL((attn_bwd_dq_f32<D, MODE>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
+  const int64_t gq = ((int64_t)nq + 255) / 256, gk = ((int64_t)nk + 255) / 256;
+  hipLaunchKernelGGL((attn_bwd_dq_f32<D, MODE>), dim3((unsigned)gq), dim3(256), 0,
                      stream, (const float*)q, (const float*)k, (const float*)v,
                      (const float*)dout, lse, delta, (float*)dq, geo, dm.T, window, scale, nq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_f32<D, MODE>), dim3((unsigned)((nk + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((attn_bwd_dkdv_f32<D, MODE>), dim3((unsigned)gk), dim3(256),
                      0, stream, (const float*)q, (const float*)k, (const float*)v,
                      (const float*)dout, lse, delta, (float*)dk, (float*)dv, geo, dm.H_kv, dm.T,
                      window, scale, nk);

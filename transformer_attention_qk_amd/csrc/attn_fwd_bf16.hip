@@ -48,6 +48,7 @@
 // unconditional.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -834,25 +835,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_tile(
   w.store(O, LSE, hoff, (int64_t)bh * T);
 }
 
-// Workgroups of a kernel the current device holds at once (cached per device and
-// instantiation; a benign race between threads writes the same value).
-template <typename Kern>
+// Workgroups of one kernel instantiation that the current device holds at once. Each
+// instantiation (Kern is a distinct function, so Tag is a distinct type) keeps its own per-device
+// cache; threads that race on the first query store the same value, through relaxed atomics.
+template <typename Tag, typename Kern>
 static hipError_t resident_workgroups(Kern kern, int* out) {
   constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices && cached[dev] > 0) {
-    *out = cached[dev];
-    return hipSuccess;
+  const bool slot = dev >= 0 && dev < kMaxDevices;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return hipSuccess;
+    }
   }
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
   if (e != hipSuccess) return e;
   const int n = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-  if (dev >= 0 && dev < kMaxDevices) cached[dev] = n;
+  if (slot) cached[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return hipSuccess;
 }
@@ -876,7 +882,8 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   if constexpr (D <= 64) {
     int resident = 0;
-    hipError_t e = resident_workgroups(attn_fwd_bf16_stream<D, MODE, QKN>, &resident);
+    struct Tag {};
+    hipError_t e = resident_workgroups<Tag>(attn_fwd_bf16_stream<D, MODE, QKN>, &resident);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
     hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN>), dim3(grid), dim3(256), 0, stream,
