@@ -64,7 +64,9 @@ enum {
   ATTN_ERR_ALIAS = 7,       /* out or lse overlaps an input it must not overlap */
   ATTN_ERR_ARG = 8,         /* another argument is out of range (eps, base, pattern, n_layer,
                                layout) */
-  ATTN_ERR_HIP = 9          /* the HIP runtime refused the launch */
+  ATTN_ERR_HIP = 9,         /* the HIP runtime refused the launch */
+  ATTN_ERR_SCRATCH = 10     /* an allocation-free call needs more scratch than the library's
+                               fixed device array (ATTN_DECODE_SCRATCH_BYTES) holds */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -347,6 +349,25 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
 int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
                    void* out, float* lse, void* workspace, long long workspace_bytes, int B,
                    int H, int H_kv, int S, int d, int layout, int window, int dtype, void* stream);
+
+/*
+ * attn_decode_ex for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ * results, with the split partials in a fixed device array of ATTN_DECODE_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends, instead of a caller workspace.
+ * It calls no hipMalloc, hipFree or allocating routine. Arguments, errors and results are those
+ * of attn_decode_ex without workspace / workspace_bytes; a shape whose
+ * attn_decode_workspace_bytes exceeds ATTN_DECODE_SCRATCH_BYTES is ATTN_ERR_SCRATCH (nothing is
+ * enqueued). Every call on a GPU shares that GPU's array: calls that may overlap on one GPU
+ * (different streams, or threads without ordering) race and must be serialised by the caller,
+ * e.g. by issuing them on one stream. Nothing needs clearing between calls: each call writes
+ * every slot it later reads. The first call on a device looks up the array's address
+ * (hipGetSymbolAddress) and keeps it.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES (8LL << 20)
+int attn_decode_noalloc_ex(const void* q, const void* k_cache, const void* v_cache,
+                           const int* lengths, void* out, float* lse, int B, int H, int H_kv,
+                           int S, int d, int layout, int window, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,8 @@ def test_header_declares_the_expected_entry_points():
             "attn_rope_table", "attn_strerror", "attn_sssl_windows", "attn_version",
             "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_qknorm_rope_bwd", "attn_decode",
             "attn_decode_ex", "attn_decode_workspace_bytes", "attn_value_gate_ex",
-            "attn_fwd_qknorm_ve_ex", "attn_value_gate_bwd_ex"} <= set(names)
+            "attn_fwd_qknorm_ve_ex", "attn_value_gate_bwd_ex",
+            "attn_decode_noalloc_ex"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -658,3 +659,52 @@ DEC_CASES = [
 @pytest.mark.parametrize("name,kw,code", DEC_CASES, ids=[c[0] for c in DEC_CASES])
 def test_decode_rejects_before_any_hip_call(lib, name, kw, code):
     assert _dec(lib, **kw) == code, name
+
+
+def _dec_noalloc(lib, **kw):
+    a = dict(_DC, B=2, H=4, H_kv=2, S=300, d=64, layout=0, window=-1, dtype=_lib.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_decode_noalloc_ex(a["q"], a["k"], a["v"], a["len"], a["out"], a["lse"],
+                                      a["B"], a["H"], a["H_kv"], a["S"], a["d"], a["layout"],
+                                      a["window"], a["dtype"], None)
+
+
+# The largest (B, H) whose workspace fits the fixed scratch at d = 128 with one split per head
+# (S = 128 keys): B * H * 130 * 4 bytes <= 8 MiB.
+_SCRATCH_HEADS = _lib.ATTN_DECODE_SCRATCH_BYTES // (130 * 4)
+
+DEC_NOALLOC_CASES = [
+    ("null q", dict(q=None), _lib.ATTN_ERR_NULL),
+    ("null out", dict(out=None), _lib.ATTN_ERR_NULL),
+    ("dtype 5", dict(dtype=5), _lib.ATTN_ERR_DTYPE),
+    ("bf16 d=16", dict(d=16), _lib.ATTN_ERR_HEAD_DIM),
+    ("S=0", dict(S=0), _lib.ATTN_ERR_SHAPE),
+    ("H_kv=3", dict(H_kv=3), _lib.ATTN_ERR_SHAPE),
+    ("layout 3", dict(layout=3), _lib.ATTN_ERR_ARG),
+    ("window -2", dict(window=-2), _lib.ATTN_ERR_WINDOW),
+    ("misaligned out", dict(out=_DC["out"] + 8), _lib.ATTN_ERR_ALIGN),
+    ("out is q", dict(out=_DC["q"]), _lib.ATTN_ERR_ALIAS),
+    ("lse over k", dict(lse=_DC["k"] + 64), _lib.ATTN_ERR_ALIAS),
+    ("workspace past the scratch", dict(B=1, H=_SCRATCH_HEADS + 1, H_kv=1, S=128, d=128,
+                                        **{n: (i + 1) << 32 for i, n in enumerate(_DC)}),
+     _lib.ATTN_ERR_SCRATCH),
+    ("workspace at the scratch limit, out over q",
+     dict({n: (i + 1) << 32 for i, n in enumerate(_DC)}, B=1, H=_SCRATCH_HEADS, H_kv=1, S=128,
+          d=128, out=1 << 32), _lib.ATTN_ERR_ALIAS),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code", DEC_NOALLOC_CASES, ids=[c[0] for c in DEC_NOALLOC_CASES])
+def test_decode_noalloc_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _dec_noalloc(lib, **kw) == code, name
+
+
+def test_decode_noalloc_scratch_limit_matches_workspace_sizes(lib):
+    # the shape one head past the limit needs more than the scratch; the limit itself fits
+    assert lib.attn_decode_workspace_bytes(1, _SCRATCH_HEADS, 128, 128, -1) <= \
+        _lib.ATTN_DECODE_SCRATCH_BYTES
+    assert lib.attn_decode_workspace_bytes(1, _SCRATCH_HEADS + 1, 128, 128, -1) > \
+        _lib.ATTN_DECODE_SCRATCH_BYTES
+    assert "scratch" in lib.attn_strerror(_lib.ATTN_ERR_SCRATCH).decode()
+

@@ -55,6 +55,7 @@ SIGNATURES = {
     "attn_decode_workspace_bytes": (ctypes.c_longlong, [c_int] * 5),
     "attn_decode": (c_int, [c_void_p] * 7 + [ctypes.c_longlong] + [c_int] * 6 + [c_void_p]),
     "attn_decode_ex": (c_int, [c_void_p] * 7 + [ctypes.c_longlong] + [c_int] * 8 + [c_void_p]),
+    "attn_decode_noalloc_ex": (c_int, [c_void_p] * 6 + [c_int] * 8 + [c_void_p]),
 }
 
 # storage orders (attn_layout)
@@ -72,6 +73,10 @@ ATTN_ERR_WINDOW = 6
 ATTN_ERR_ALIAS = 7
 ATTN_ERR_ARG = 8
 ATTN_ERR_HIP = 9
+ATTN_ERR_SCRATCH = 10
+
+# fixed device scratch of attn_decode_noalloc_ex (ATTN_DECODE_SCRATCH_BYTES)
+ATTN_DECODE_SCRATCH_BYTES = 8 << 20
 
 ATTN_BF16 = 0
 ATTN_F32 = 1

@@ -13,6 +13,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // far above any device memory
 constexpr int64_t kMaxGrid = 0x7fffffff;
 constexpr int64_t kMaxItems = kMaxGrid;  // work items (workgroups) of one attention launch
 
+static_assert(attn::kDecodeScratchBytes == ATTN_DECODE_SCRATCH_BYTES,
+              "the header states the decode scratch size");
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -74,6 +77,8 @@ const char* attn_strerror(int code) {
     case ATTN_ERR_ALIAS: return "an output overlaps an input it must not overlap";
     case ATTN_ERR_ARG: return "argument out of range";
     case ATTN_ERR_HIP: return "HIP launch failed";
+    case ATTN_ERR_SCRATCH:
+      return "the call needs more scratch than the library's fixed device array holds";
     default: return "unknown attn status code";
   }
 }
@@ -500,31 +505,36 @@ long long attn_decode_workspace_bytes(int B, int H, int S, int d, int window) {
   return (long long)attn::decode_workspace_bytes(B, H, S, d, window);
 }
 
-int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
-                   void* out, float* lse, void* workspace, long long workspace_bytes, int B,
-                   int H, int H_kv, int S, int d, int layout, int window, int dtype,
-                   void* stream) {
-  if (!q || !k_cache || !v_cache || !out || !workspace) return ATTN_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Checks of one decode call shared by attn_decode_ex and attn_decode_noalloc_ex. workspace is the
+// caller's buffer (ws_bytes long) or, for the allocation-free call, nullptr (nothing to check).
+int check_decode(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
+                 const void* out, const float* lse, const void* workspace, long long ws_bytes,
+                 int B, int H, int H_kv, int S, int d, int layout, int window, int dtype,
+                 attn::Dims* dm, int64_t* need) {
+  if (!q || !k_cache || !v_cache || !out) return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (dtype == ATTN_BF16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  attn::Dims dm;
   int64_t n_q = 0, n_kv = 0;
-  if (int rc = check_dims(B, H, H_kv, S, d, layout, &dm, &n_q, &n_kv)) return rc;
+  if (int rc = check_dims(B, H, H_kv, S, d, layout, dm, &n_q, &n_kv)) return rc;
   if (window < -1) return ATTN_ERR_WINDOW;
   const void* vec[] = {q, k_cache, v_cache, out, workspace};
   for (const void* t : vec)
-    if (!aligned16(t)) return ATTN_ERR_ALIGN;
+    if (t && !aligned16(t)) return ATTN_ERR_ALIGN;
   if ((lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) ||
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_ALIGN;
-  const int64_t need = attn::decode_workspace_bytes(B, H, S, d, window);
-  if (workspace_bytes < need) return ATTN_ERR_ARG;
+  *need = attn::decode_workspace_bytes(B, H, S, d, window);
+  if (workspace && ws_bytes < *need) return ATTN_ERR_ARG;
   const int64_t eb = elem_bytes(dtype);
   const int64_t qb = (int64_t)B * H * d * eb, kb = n_kv * eb;
   // Written: out, lse, workspace; none overlaps another buffer.
   const void* bufs[] = {q, k_cache, v_cache, lengths, out, lse, workspace};
-  const int64_t len[] = {qb, kb, kb, (int64_t)B * 4, qb, (int64_t)B * H * 4, need};
+  const int64_t len[] = {qb, kb, kb, (int64_t)B * 4, qb, (int64_t)B * H * 4, *need};
   for (int w = 4; w < 7; ++w) {
     if (!bufs[w]) continue;
     for (int o = 0; o < 7; ++o)
@@ -532,8 +542,43 @@ int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, cons
   }
   if ((int64_t)B * H_kv * attn::decode_splits(B, H, S, d, window) > kMaxGrid)
     return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int* lengths,
+                   void* out, float* lse, void* workspace, long long workspace_bytes, int B,
+                   int H, int H_kv, int S, int d, int layout, int window, int dtype,
+                   void* stream) {
+  if (!workspace) return ATTN_ERR_NULL;
+  attn::Dims dm;
+  int64_t need = 0;
+  if (int rc = check_decode(q, k_cache, v_cache, lengths, out, lse, workspace, workspace_bytes, B,
+                            H, H_kv, S, d, layout, window, dtype, &dm, &need))
+    return rc;
   const hipError_t e = attn::launch_attn_decode(q, k_cache, v_cache, lengths, out, lse, workspace,
                                                 dm, window, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_decode_noalloc_ex(const void* q, const void* k_cache, const void* v_cache,
+                           const int* lengths, void* out, float* lse, int B, int H, int H_kv,
+                           int S, int d, int layout, int window, int dtype, void* stream) {
+  attn::Dims dm;
+  int64_t need = 0;
+  if (int rc = check_decode(q, k_cache, v_cache, lengths, out, lse, nullptr, 0, B, H, H_kv, S, d,
+                            layout, window, dtype, &dm, &need))
+    return rc;
+  if (need > attn::kDecodeScratchBytes) return ATTN_ERR_SCRATCH;
+  // The partial kernel writes every split slot the merge then reads, so the scratch needs no
+  // clearing between calls.
+  void* ws = nullptr;
+  if (attn::decode_scratch(&ws) != hipSuccess) return ATTN_ERR_HIP;
+  const hipError_t e = attn::launch_attn_decode(q, k_cache, v_cache, lengths, out, lse, ws, dm,
+                                                window, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

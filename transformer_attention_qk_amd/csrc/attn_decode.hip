@@ -21,6 +21,8 @@
 // The weights stay fp32 (no bf16 rounding), every sum is fp32, out is rounded once.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -270,6 +272,30 @@ __global__ __launch_bounds__(256) void attn_decode_merge(const float* __restrict
     out[(int64_t)bh * D + e] = (Elem)(ot * (1.0f / Lt));
     if (e == 0 && lse != nullptr) lse[bh] = (Mt + __log2f(Lt)) * kLn2;
   }
+}
+
+// Scratch of the allocation-free decode entry point: the split partials live in this fixed
+// device array (one copy per GPU, held until the process ends) instead of a caller workspace.
+// Host code never passes the array's name to a kernel: it is a host-side stand-in there. The
+// device address comes from hipGetSymbolAddress, once per device, and is kept below.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);  // racing threads store the same address
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 int decode_splits(int B, int H, int S, int d, int window) {

@@ -117,4 +117,9 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const
                               void* out, float* lse, void* ws, const Dims& dm, int window,
                               int dtype, hipStream_t stream);
 
+// Decode scratch for callers that cannot allocate: a static device array of
+// kDecodeScratchBytes per GPU. decode_scratch returns its device address on the current device.
+constexpr int64_t kDecodeScratchBytes = int64_t(8) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace attn

@@ -432,3 +432,41 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                             _stream_handle())
     _lib.check("attn_decode_ex", rc)
     return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   lengths: torch.Tensor | None = None, window: int = -1,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   layout: str = "bhtd"):
+    """``decode`` through the allocation-free entry point (attn_decode_noalloc_ex): the split
+    partials use the library's fixed device scratch instead of a workspace. With ``out`` and
+    ``lse`` given, nothing is allocated here either."""
+    lib = _lib.load()
+    _require(q, "q")
+    if q.dim() != 3 or q.dtype not in _DTYPES:
+        raise ValueError("q must be [B, H, d] bf16 or fp32")
+    _require(k_cache, "k_cache", dtype=q.dtype)
+    _require(v_cache, "v_cache", k_cache.shape, q.dtype)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be 4-d")
+    B, H, d = q.shape
+    if layout == "bhtd":
+        _, H_kv, S, _ = k_cache.shape
+    elif layout == "bthd":
+        _, S, H_kv, _ = k_cache.shape
+    else:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}, got {layout!r}")
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or H % H_kv:
+        raise ValueError("k_cache must hold the batch, head dim and a kv head count dividing H")
+    if lengths is not None:
+        _require(lengths, "lengths", (B,), torch.int32)
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", q.shape, q.dtype)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _require(lse, "lse", (B, H), torch.float32)
+    rc = lib.attn_decode_noalloc_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths),
+                                    _ptr(out), _ptr(lse), B, H, H_kv, S, d, _LAYOUTS[layout],
+                                    int(window), _DTYPES[q.dtype], _stream_handle())
+    _lib.check("attn_decode_noalloc_ex", rc)
+    return out, lse
