@@ -351,22 +351,40 @@ struct WaveTile {
         if (!full(t, kb)) {
           // Register r holds key b0 + c_r with c_r = 8 (r / 4) + r % 4. With dq = qi - b0, the
           // key is visible iff c_r <= dq (causal), c_r >= dq - window (window) and
-          // c_r <= T - 1 - b0 (sequence end): one upper limit per lane, so each register needs
-          // one compare (two with a window) whose result is used at once.
-          const int b0 = t * C::BN + 32 * kb + 4 * hi;
+          // c_r <= T - 1 - b0 (sequence end): one upper and one lower limit per lane. The block
+          // needs the upper test only if it reaches past the wave's first query or the sequence
+          // end, and the lower one only if it starts before the wave's last query's window; a
+          // window of 32 or more keys never needs both in one block, so each register takes one
+          // compare there.
+          const int bb = t * C::BN + 32 * kb;  // the block's first key (wave-uniform)
+          const bool need_hi = (causal && bb + 31 > qw0) || (bb + 32 > T);
+          const bool need_lo = (MODE == kCausalWindow) && (bb < qw0 + 31 - window);
+          const int b0 = bb + 4 * hi;
           const int dq = qi - b0;
           int hi_c = causal ? dq : 0x7fffffff;
-          if (t * C::BN + 32 * kb + 32 > T) hi_c = min(hi_c, T - 1 - b0);  // wave-uniform test
+          if (bb + 32 > T) hi_c = min(hi_c, T - 1 - b0);
           int lo_c = dq - window;
           // Opaque to the optimiser: otherwise it hoists the 16-32 per-register lane masks of a
           // loop-invariant edge out of the loops and spills them.
           asm volatile("" : "+v"(hi_c), "+v"(lo_c));
+          if (need_hi && need_lo) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 8 * (r >> 2) + (r & 3);
-            bool vis = c <= hi_c;
-            if constexpr (MODE == kCausalWindow) vis = vis & (c >= lo_c);
-            sa[kb][r] = vis ? sa[kb][r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+              const int c = 8 * (r >> 2) + (r & 3);
+              sa[kb][r] = ((c <= hi_c) & (c >= lo_c)) ? sa[kb][r] : -INFINITY;
+            }
+          } else if (need_hi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = 8 * (r >> 2) + (r & 3);
+              sa[kb][r] = (c <= hi_c) ? sa[kb][r] : -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = 8 * (r >> 2) + (r & 3);
+              sa[kb][r] = (c >= lo_c) ? sa[kb][r] : -INFINITY;
+            }
           }
         }
       }
@@ -458,6 +476,67 @@ struct WaveTile {
     }
   }
 
+  // One pipelined step with a next tile: the scores of both 32-key blocks of tile t+1 (K tile at
+  // kbuf) go to the matrix cores while the vector ALUs exponentiate tile t's scores (cur), then
+  // P(t) V(t) (V tile at vbuf). The LDS reads are issued ahead of the products that use them:
+  // all K fragments first, then the transposing V reads spread over the score products, so no
+  // product waits on a read issued right before it. The instruction order is fixed with
+  // scheduling groups (one score product, then a share of the exponentials and V reads).
+  __device__ __forceinline__ void step_pipelined(const char* kbuf, const char* vbuf,
+                                                 const f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr int NS = 2 * C::KSTEPS;       // score products
+    constexpr int NV = 2 * 2 * C::DB * 2;   // transposing V reads (two per P V product)
+    bf16x8 kf[2][C::KSTEPS];
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[kb][s] = *reinterpret_cast<const bf16x8*>(kbuf + 32 * kb * C::ROW_BYTES + k_row_off +
+                                                     16 * ((2 * s + hi) ^ k_swz));
+    __builtin_amdgcn_sched_barrier(0);
+    u32x2 vp[2][2][C::DB][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int row = 32 * kb + 16 * tt + 8 * u + 4 * hi + v_a;
+            const int c = 4 * db + 2 * v_g1 + (v_b >> 1);
+            vp[kb][tt][db][u] =
+                ds_read_tr16_b64(vbuf + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
+          }
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[s],
+                                                          s == 0 ? f32x16{} : nxt[kb], 0, 0, 0);
+    bf16x8 pf[2][2];
+    exps(cur, pf);
+    // Order: per score product, its share of the V reads and of the vector work.
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, NV / NS, 0);     // V reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 64 / NS, 0);     // vector ALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const u32x4 a4{vp[kb][tt][db][0][0], vp[kb][tt][db][0][1], vp[kb][tt][db][1][0],
+                         vp[kb][tt][db][1][1]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                              pf[kb][tt], oacc[db], 0, 0, 0);
+        }
+  }
+
   // Unpipelined tile: scores, mask and maximum, update, exponentials, P V.
   __device__ __forceinline__ void whole_tile(const char* kbuf, const char* vbuf, int t) {
     f32x16 sa[2];
@@ -527,8 +606,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   const char* qbuf = smem + C::NSTAGE * 2 * C::TILE_BYTES;
 
-  // Items of this workgroup: heaviest-first ranks dealt out in snake order.
-  auto rank_of = [&](int k) { return k * P + ((k & 1) ? (P - 1 - g) : g); };
+  // Items of this workgroup: heaviest-first ranks dealt out in snake order. Workgroup g runs on
+  // XCD g mod 8 (round-robin dispatch), and rank r = qb * BH + bh sits at position r mod P of its
+  // round; when P is a multiple of 8 the odd rounds reverse the order within each class of
+  // workgroups g = c mod 8, so the position keeps its class and, when BH is a multiple of 8 too,
+  // every query block of a head runs on one XCD and its K/V tiles are cached in one L2.
+  const int g_rev = ((P & 7) == 0) ? ((((P >> 3) - 1 - (g >> 3)) << 3) + (g & 7)) : (P - 1 - g);
+  auto rank_of = [&](int k) { return k * P + ((k & 1) ? g_rev : g); };
   auto decode = [&](int rank, int& bh, int& q0, int& tb, int& te) {
     const int qb = (int)fd_bh.div((uint32_t)rank);
     bh = rank - qb * BH;
@@ -612,28 +696,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     }
   };
 
-  // Workgroup prologue: stream tiles 0 and 1 and the first item's Q (and, QKN, its rotation
-  // rows into the K half of the last stage, which the stream reaches only in the first tile
-  // step), then tile 2 in flight. The wait is a compiler-visible s_waitcnt vmcnt(0), so the
-  // compiler puts no wait of its own inside the loop (such a wait would also stall on the tiles
-  // in flight).
+  // Workgroup prologue: the first item's rotation rows (QKN; into the K half of the last stage,
+  // which the stream reaches only in the first tile step) and its Q block, then tiles 0 and 1 of
+  // the stream, all by direct loads. Only the rows, the Q block and tile 0 are waited for here;
+  // tile 1 lands while the first item's first scores are formed (it is waited for after them),
+  // and tile 2 goes out once the Q fragments are formed.
   int k = 0, bh, q0, tb, te;
   decode(rank_of(0), bh, q0, tb, te);
   w.set_item(q0);
-  issue_next();
-  issue_next();
   if constexpr (QKN) dma_rope(q0, C::NSTAGE - 1);
+  dma_q(bh, q0);
+  issue_next();
+  issue_next();
+  wait_vmcnt<C::DMA_PER_TILE>();
+  __syncthreads();
   typename WaveTile<D, MODE, QKN>::Rope rope;
   {
-    bf16x8 xf[C::KSTEPS];
-    w.load_q_global(head_rsrc(Q + geo.q_head(bh), q_slab), q0, xf);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
     w.rope_from_lds(smem + (C::NSTAGE - 1) * (2 * C::TILE_BYTES), rope);
+    bf16x8 xf[C::KSTEPS];
+    w.load_q_lds(qbuf, xf);
     w.set_q(xf, rope, q0, eps);
   }
-  // (QKN) every wave has read the rotation rows before the first tile step loads into that stage
-  if constexpr (QKN) __syncthreads();
+  // Every wave has read its Q rows and rotation rows before any wave loads into the Q buffer (the
+  // first item's last step) or into that stage (the first tile step).
+  __syncthreads();
   issue_next();
   unsigned st_comp = 0;  // stage of the tile being consumed
 
@@ -651,6 +737,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
         mx = w.template mask_max<false>(tb, sacc[0]);
       }
       w.decide(mx);
+    }
+    if (k == 0) {
+      // The workgroup's first item: tile 1 of the stream, issued in the workgroup prologue, has
+      // landed (tile 2 may still be in flight) before any wave reads it.
+      wait_vmcnt<C::DMA_PER_TILE>();
+      __syncthreads();
     }
     const int rank_n = rank_of(k + 1);
     const bool more = rank_n < n_items;
@@ -686,9 +778,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       // fully visible; tile t's blocks that the wave does not see hold -inf scores (zero
       // weights), so its exponentials and P V need no guards.
       if constexpr (has_next) {
+#ifdef ATTN_OLD_STEP
         w.template scores<true, true>(kn, t + 1, nxt);
         w.exps(cur, pf);
         w.template pv<true>(vc, t, pf);
+#else
+        w.step_pipelined(kn, vc, cur, nxt);
+#endif
         if (w.fast(t + 1))
           mx = w.template mask_max<true>(t + 1, nxt);
         else
