@@ -216,17 +216,21 @@ struct WaveTile {
       constexpr int RB = D * 2;  // bytes of one staged row (d/2 floats)
       const int ln = lane_now();
       const int l = ln & 31, col = 32 * (ln >> 5);  // byte offset of column 8 hi
-      const char* cb = rope_lds + (2 * wave + (l >> 4)) * RB + col;
-      const char* cl = rope_lds + (8 + (l & 15)) * RB + col;
+      // Rows are stored with their 16-byte chunks rotated by swz_rope (see the staging loads).
+      const int rb = 2 * wave + (l >> 4), rl = 8 + (l & 15);
+      const char* cb = rope_lds + rb * RB;
+      const char* cl = rope_lds + rl * RB;
+      const int sb = swz_rope<D>(rb), sl = swz_rope<D>(rl), c0 = col / 16;
 #pragma unroll
       for (int s = 0; s < C::KSTEPS / 2; ++s)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int o = 64 * s + 16 * h;
-          const f32x4 c_b = *reinterpret_cast<const f32x4*>(cb + o);
-          const f32x4 s_b = *reinterpret_cast<const f32x4*>(cb + C::ROPE_PART + o);
-          const f32x4 c_l = *reinterpret_cast<const f32x4*>(cl + o);
-          const f32x4 s_l = *reinterpret_cast<const f32x4*>(cl + C::ROPE_PART + o);
+          const int c = c0 + 4 * s + h;  // logical chunk of columns 16 s + 8 hi + 4 h .. +4
+          const int ob = 16 * (c ^ sb), ol = 16 * (c ^ sl);
+          const f32x4 c_b = *reinterpret_cast<const f32x4*>(cb + ob);
+          const f32x4 s_b = *reinterpret_cast<const f32x4*>(cb + C::ROPE_PART + ob);
+          const f32x4 c_l = *reinterpret_cast<const f32x4*>(cl + ol);
+          const f32x4 s_l = *reinterpret_cast<const f32x4*>(cl + C::ROPE_PART + ol);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             r.c[s][h][e] = fmaf(c_b[e], c_l[e], -(s_b[e] * s_l[e]));
@@ -656,9 +660,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     for (int r = w.wave; r < C::ROPE_RUNS; r += 4) {  // wave-uniform
       const int part = r / RPP, run = r % RPP;
       const int p = run * 64 + w.lane;
+      // staged row row_i, physical chunk col holds logical chunk col ^ swz_rope(row_i)
       const int row_i = p / CPR, col = p % CPR;
       const int row = row_i < 8 ? min(q0 + 16 * row_i, T - 1) : min(row_i - 8, T - 1);
-      const uint32_t off = row_i < C::ROPE_ROWS ? (uint32_t)(row * (D * 2) + 16 * col) : kOutOfRange;
+      const uint32_t off = row_i < C::ROPE_ROWS
+                               ? (uint32_t)(row * (D * 2) + 16 * (col ^ swz_rope<D>(row_i)))
+                               : kOutOfRange;
       dma16(part ? rs : rc, base + part * C::ROPE_PART + run * 1024, off);
     }
   };

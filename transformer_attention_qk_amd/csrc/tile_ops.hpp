@@ -22,6 +22,16 @@ __device__ __forceinline__ int swz_v(int r) {
   else return (r & 3) << 2;
 }
 
+// Same for the staged rows of rotation factors (d/2 fp32 per row, CPR = d/8 chunks): a half-wave
+// reads one logical chunk of 16 consecutive rows, RPL of which share a 256-byte LDS line, so the
+// chunk is rotated by the row's line index to put the 16 reads on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_rope(int r) {
+  constexpr int CPR = D / 8;
+  constexpr int RPL = (256 / (CPR * 16)) > 0 ? 256 / (CPR * 16) : 1;
+  return (r / RPL) % CPR;
+}
+
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs: 32-bit data format.
