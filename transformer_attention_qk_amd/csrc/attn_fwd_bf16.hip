@@ -552,21 +552,38 @@ struct WaveTile {
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 for this wave's queries of head offset hoff.
+  // Lane l and l + 32 hold the two 8-byte halves of each 16-byte chunk (columns 32 db + 8 g ..
+  // +8) of row qi; one v_permlane32_swap per word gathers chunk 2m into lane l and chunk 2m + 1
+  // into lane l + 32, so each store writes 16 bytes per lane, 32 contiguous bytes per row.
   __device__ __forceinline__ void store(bf16* O, float* LSE, int64_t hoff, int64_t lse_off) {
     const float l_tot = pair_sum(l_run0 + l_run1);
+    const float inv = 1.0f / l_tot;
+    u32x4 ch[C::DB][2];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint32_t x[2], y[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int g0 = 2 * m, g1 = 2 * m + 1;
+          x[k] = pack_bf16x2(oacc[db][4 * g0 + 2 * k] * inv, oacc[db][4 * g0 + 2 * k + 1] * inv);
+          y[k] = pack_bf16x2(oacc[db][4 * g1 + 2 * k] * inv, oacc[db][4 * g1 + 2 * k + 1] * inv);
+          // lanes < 32 get (own x, partner's x), lanes >= 32 (partner's y, own y)
+          const auto sw = __builtin_amdgcn_permlane32_swap(x[k], y[k], false, false);
+          x[k] = sw[0];
+          y[k] = sw[1];
+        }
+        ch[db][m] = u32x4{x[0], x[1], y[0], y[1]};
+      }
+    }
     if (qi < T) {
-      const float inv = 1.0f / l_tot;
       bf16* orow = O + hoff + (int64_t)qi * (q_rs / 2);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-          w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * hi) = w;
-        }
-      }
+        for (int m = 0; m < 2; ++m)
+          *reinterpret_cast<u32x4*>(orow + 32 * db + 16 * m + 8 * hi) = ch[db][m];
       if (hi == 0 && LSE != nullptr) LSE[lse_off + qi] = (m_run + __log2f(l_tot)) * kLn2;
     }
   }
