@@ -94,58 +94,89 @@ def source_sha(paths: list[str]) -> str:
     return h.hexdigest()
 
 
-def measured_traffic() -> float | None:
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+def measured_counter(key: str = "traffic_bytes_per_launch") -> float | None:
+    """A figure of the committed rocprofv3 counter summary of the attention kernel (HBM bytes per
+    launch, or the MFMA busy fraction), if the summary was taken on the current kernel source;
+    else None."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
         return None
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    val = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", text)
     if not sha or not val or sha.group(1) != source_sha(ATTN_SOURCES):
         return None
     return float(val.group(1))
 
 
-def cpu_baseline(w, layer_inputs, windows: list[int], budget_s: float) -> dict:
-    """The fp64 oracle on a bounded sample of the same workload: whole heads, all layers, in
-    (b, h) order, until the time budget is spent. Returns TFLOP/s on the same unmasked-FLOP
-    numerator as the GPU. layer_inputs: each layer's CPU q, k, v in [B, H, T, d] order."""
-    import numpy as np
-    import torch
-    from threadpoolctl import threadpool_info
+def measured_traffic() -> float | None:
+    return measured_counter("traffic_bytes_per_launch")
+
+
+# What the pages report about the hardware they ran on (context only; none of them gives an
+# attention throughput figure).
+PAGES_CONTEXT = {
+    "attention_throughput_on_pages": None,
+    "autoresearch_hardware": "H100 (the train.py listing's experiments; its MFU uses a 989.5 "
+                             "TFLOP/s bf16 peak and reports 39.8 % for the whole model's training)",
+    "andrea_hardware": "RTX 4090, or an RTX 3060 (the ANDREA family's training)",
+    "note": "another machine's whole-model figures, not an attention-kernel target; vs_baseline "
+            "stays null",
+}
+
+
+# Inputs of the CPU-baseline workers, set in the parent before the pool forks (so the workers
+# inherit them instead of receiving pickled copies): per layer (q, k, v) fp64 [B, H, T, d], the
+# windows and the head count per batch.
+_CPU_WORK = None
+
+
+def _cpu_head(bh: int) -> tuple[int, float]:
+    """One (batch, head) of every layer through the fp64 oracle, single-threaded BLAS; returns
+    (unmasked FLOPs, CPU seconds)."""
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
-    flops = 0
-    heads = 0
-    elapsed = 0.0
-    for b in range(w.B):
-        for h in range(w.H):
-            per_layer = [tuple(x[b:b + 1, h:h + 1].to(torch.float64).numpy() for x in li)
-                         for li in layer_inputs]
-            t0 = time.perf_counter()
-            for (q, k, v), W in zip(per_layer, windows):
-                oracle.attention_layer(q, k, v, window=W)
-            elapsed += time.perf_counter() - t0
-            flops += sum(attn_flops(1, 1, w.T, w.d, W) for W in windows)
-            heads += 1
-            if elapsed >= budget_s:
-                break
-        if elapsed >= budget_s:
-            break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    del np
+    layers, windows, H, T, d = _CPU_WORK
+    b, h = divmod(bh, H)
+    t0 = time.process_time()
+    with threadpool_limits(1):
+        for (q, k, v), W in zip(layers, windows):
+            oracle.attention_layer(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                   window=W)
+    return sum(attn_flops(1, 1, T, d, W) for W in windows), time.process_time() - t0
+
+
+def cpu_baseline(w, layer_inputs, windows: list[int], workers: int) -> dict:
+    """The fp64 oracle on the same workload: a process pool over the (batch, head) pairs, one
+    BLAS thread per worker, every head of every layer. Returns TFLOP/s on the same
+    unmasked-FLOP numerator as the GPU over the pool's wall time. Must run before the process
+    touches the GPU (the pool forks). layer_inputs: each layer's CPU q, k, v [B, H, T, d]."""
+    import multiprocessing
+
+    global _CPU_WORK
+    _CPU_WORK = ([tuple(x.to(dtype=__import__("torch").float64).numpy() for x in li)
+                  for li in layer_inputs], windows, w.H, w.T, w.d)
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        parts = pool.map(_cpu_head, range(w.B * w.H), chunksize=1)
+    elapsed = time.perf_counter() - t0
+    _CPU_WORK = None
+    flops = sum(f for f, _ in parts)
+    cpu_s = sum(c for _, c in parts)
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"{heads} of {w.B * w.H} heads (b, h order), all {len(windows)} layers of "
-                   f"{w.name}: fp64 QK-norm + RoPE + attention, {elapsed:.1f} s; "
-                   f"cores = BLAS threads; host has {len(os.sched_getaffinity(0))} cores"),
+        "sample": (f"all {w.B * w.H} heads of all {len(windows)} layers of {w.name} (fp64 QK-norm "
+                   f"+ RoPE + attention), a pool of {workers} processes with one BLAS thread "
+                   f"each over (batch, head) pairs: {elapsed:.2f} s wall, {cpu_s:.1f} s of CPU; "
+                   f"host affinity {len(os.sched_getaffinity(0))} cores"),
         "seconds": elapsed,
+        "cpu_seconds": cpu_s,
     }
 
 
@@ -159,7 +190,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward, decode and value-gate timings")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="CPU-baseline processes (default: the host's cores, at most 16)")
     ap.add_argument("--only", default=None,
                     choices=["attn", "kprologue", "attn_unfused", "prologue", "decode", "bwd"])
     ap.add_argument("--copy-calibration", action="store_true")
@@ -175,6 +207,21 @@ def main() -> int:
     import torch
 
     from transformer_attention_qk_amd import _lib, inputs, ops
+
+    # The CPU baseline runs first, before anything touches the GPU, because its process pool
+    # forks. Its inputs are the same seeded tensors the GPU step uses.
+    cpu_result = None
+    if not (args.no_cpu_baseline or args.only or args.copy_calibration):
+        names0 = [x.name for x in inputs.WORKLOADS] + [inputs.MODEL_DEFAULT.name]
+        if args.workload in names0:
+            import oracle
+            i0 = names0.index(args.workload)
+            w0 = inputs.workload(i0)
+            if w0.dtype == "bf16":
+                win0 = oracle.sssl_windows(w0.T, w0.n_layer, w0.pattern)
+                workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+                cpu_result = cpu_baseline(w0, [inputs.make_qkv(i0, l) for l in range(len(win0))],
+                                          win0, workers)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -213,11 +260,9 @@ def main() -> int:
 
     # Inputs resident in HBM, one set of buffers per layer (drawn in [B, H, T, d] order, stored
     # in the layout the workload runs in).
-    q, k, v, qn, kn, out, lse, cpu_inputs = ([] for _ in range(8))
+    q, k, v, qn, kn, out, lse = ([] for _ in range(7))
     for l in range(L):
         ql, kl, vl = inputs.make_qkv(index, l)
-        if not args.no_cpu_baseline:
-            cpu_inputs.append((ql, kl, vl))
         for dst, x in ((q, ql), (k, kl), (v, vl)):
             x = x.cuda()
             dst.append((x.transpose(1, 2) if layout == "bthd" else x).contiguous())
@@ -425,6 +470,22 @@ def main() -> int:
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     cold_ms = [time_alone(l, lambda: flush.fill_(1)) for l in range(L)]
     del flush
+    # A plain device copy of the k-only prologue's bytes (one k tensor read, one written), the
+    # rate an HBM-bound read-and-write pass reaches on this part, beside the prologue's.
+    copy_src = k[0].clone()
+    copy_dst = torch.empty_like(copy_src)
+    copy_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for _ in range(3):
+        copy_dst.copy_(copy_src)
+    torch.cuda.synchronize()
+    for a_, b_ in copy_ev:
+        a_.record()
+        copy_dst.copy_(copy_src)
+        b_.record()
+    torch.cuda.synchronize()
+    copy_ms = sum(a_.elapsed_time(b_) for a_, b_ in copy_ev) / args.steps
+    del copy_src, copy_dst
     # The two-call path, for comparison.
     ms_per_step_unfused = time_steps(step_unfused)
     pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
@@ -496,6 +557,7 @@ def main() -> int:
     pro_bytes = prologue_bytes(w.B, w.H, w.T, w.d, tensors=2)
     # the committed counter summary covers the headline workload only
     traffic = measured_traffic() if w.name == HEADLINE else None
+    mfma_busy = measured_counter("mfma_busy") if w.name == HEADLINE else None
     kernel = (f"attn_fwd_bf16_stream<{w.d}, mode, qkn=true>" if w.d <= 64
               else f"attn_fwd_bf16_tile<{w.d}, mode, qkn=true>")
 
@@ -524,6 +586,7 @@ def main() -> int:
             "flops_per_step": step_flops,
         },
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "context": PAGES_CONTEXT,
         "roofline": {
             "bound": "mfma",
             "kernel": kernel,
@@ -532,6 +595,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": None if traffic is None else int(traffic),
+            "mfma_busy": mfma_busy,
             "avg_launch_us": round(1e3 * attn_total_ms / L, 3),
             "launch_us": [round(1e3 * t, 3) for t in attn_ms],
             "flops_per_launch": flops_layer,
@@ -543,6 +607,8 @@ def main() -> int:
             "bytes_per_launch": kpro_bytes,
             "achieved_gbs": round(kpro_bytes * L / (sum(kpro_ms) * 1e-3) / 1e9, 1),
             "peak_gbs": PEAK_HBM_GBS,
+            "copy_same_bytes_us": round(1e3 * copy_ms, 3),
+            "copy_gbs": round(kpro_bytes / (copy_ms * 1e-3) / 1e9, 1),
         },
         "cache_states": {
             "note": "attention launch alone: hot = one layer's launch repeated back to back; "
@@ -598,8 +664,8 @@ def main() -> int:
             "gate_alone_avg_us": round(1e3 * sum(vg_ms) / L, 3),
             "gate_alone_gbs": round(gate_bytes * L / (sum(vg_ms) * 1e-3) / 1e9, 1),
         }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, cpu_inputs, windows, args.cpu_budget)
+    if cpu_result is not None:
+        result["cpu_baseline"] = cpu_result
     print(json.dumps(result), flush=True)
     return 0
 

@@ -37,3 +37,21 @@ def test_prologue_bytes():
     # each tensor read once and written once, bf16
     assert bench.prologue_bytes(16, 12, 1024, 64, tensors=1) == 16 * 12 * 1024 * 64 * 2 * 2
     assert bench.prologue_bytes(16, 12, 1024, 64) == 2 * bench.prologue_bytes(16, 12, 1024, 64, tensors=1)
+
+
+def test_cpu_baseline_pool_counts_every_head():
+    """The CPU baseline's process pool runs every (batch, head) of every layer through the oracle
+    and counts the same unmasked FLOPs as the GPU numerator (a small synthetic workload)."""
+    import collections
+
+    import torch
+
+    W = collections.namedtuple("W", "name B H T d")
+    w = W("tiny", 2, 3, 40, 8)
+    g = torch.Generator().manual_seed(0)
+    layers = [tuple(torch.randn(2, 3, 40, 8, generator=g) for _ in range(3)) for _ in range(2)]
+    wins = [20, 40]
+    r = bench.cpu_baseline(w, layers, wins, 2)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    flops = sum(bench.attn_flops(2, 3, 40, 8, W_) for W_ in wins)
+    assert abs(r["value"] * 1e12 * r["seconds"] - flops) <= 1e-6 * flops
