@@ -190,6 +190,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward, decode and value-gate timings")
+    ap.add_argument("--no-cache-states", action="store_true",
+                    help="skip the hot / cold cache-state runs and the two-call path (so a kernel "
+                         "trace of the run holds the in-model launches only)")
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="CPU-baseline processes (default: the host's cores, at most 16)")
     ap.add_argument("--only", default=None,
@@ -466,10 +469,12 @@ def main() -> int:
     # inputs stay in the caches); "cold" writes a 512 MiB buffer (twice the Infinity Cache)
     # before each launch. The in-model order above (k just written by the prologue) is the
     # headline state.
-    hot_ms = [time_alone(l) for l in range(L)]
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold_ms = [time_alone(l, lambda: flush.fill_(1)) for l in range(L)]
-    del flush
+    hot_ms = cold_ms = None
+    if not args.no_cache_states:
+        hot_ms = [time_alone(l) for l in range(L)]
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_ms = [time_alone(l, lambda: flush.fill_(1)) for l in range(L)]
+        del flush
     # A plain device copy of the k-only prologue's bytes (one k tensor read, one written), the
     # rate an HBM-bound read-and-write pass reaches on this part, beside the prologue's.
     copy_src = k[0].clone()
@@ -487,8 +492,9 @@ def main() -> int:
     copy_ms = sum(a_.elapsed_time(b_) for a_, b_ in copy_ev) / args.steps
     del copy_src, copy_dst
     # The two-call path, for comparison.
-    ms_per_step_unfused = time_steps(step_unfused)
-    pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
+    if not args.no_cache_states:
+        ms_per_step_unfused = time_steps(step_unfused)
+        pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
 
     def nothing_step(l):
         return 0
@@ -610,7 +616,9 @@ def main() -> int:
             "copy_same_bytes_us": round(1e3 * copy_ms, 3),
             "copy_gbs": round(kpro_bytes / (copy_ms * 1e-3) / 1e9, 1),
         },
-        "cache_states": {
+    }
+    if hot_ms is not None:
+        result["cache_states"] = {
             "note": "attention launch alone: hot = one layer's launch repeated back to back; "
                     "cold = a 512 MiB write before each launch; headline = roofline.launch_us "
                     "(in-model order, k just written by the prologue)",
@@ -618,8 +626,8 @@ def main() -> int:
             "hot_tflops": round(step_flops / (sum(hot_ms) * 1e-3) / 1e12, 3),
             "cold_launch_us": [round(1e3 * t, 3) for t in cold_ms],
             "cold_tflops": round(step_flops / (sum(cold_ms) * 1e-3) / 1e12, 3),
-        },
-        "two_call_path": {
+        }
+        result["two_call_path"] = {
             "ms_per_step": round(ms_per_step_unfused, 5),
             "value": round(step_flops / (ms_per_step_unfused * 1e-3) / 1e12, 3),
             "attn_avg_launch_us": round(1e3 * sum(attn_unf_ms) / L, 3),
@@ -627,8 +635,7 @@ def main() -> int:
             "prologue_avg_launch_us": round(1e3 * sum(pro_ms) / L, 3),
             "prologue_bytes_per_launch": pro_bytes,
             "prologue_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
-        },
-    }
+        }
     if dec_ms is not None:
         result["decode"] = {
             "note": "one generation step per layer: the newest token of each (batch, head) "
