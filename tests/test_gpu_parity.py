@@ -308,7 +308,8 @@ def test_masked_keys_have_no_influence_bitwise(d):
     v = inputs.make_random((B, H, T, d), torch.bfloat16, 23)
     for window in (-1, 70):
         out, lse = ops.attn_fwd(dev(q), dev(k), dev(v), window=window)
-        for i in (0, 5, 127, 128, 200, 399):
+        # rows at the edges of the waves' 32-row blocks, the 64-key tiles and the 128-row items
+        for i in (0, 5, 31, 32, 57, 63, 64, 95, 96, 100, 127, 128, 200, 255, 256, 383, 384, 399):
             say(f"mask perturbation d={d} W={window} row={i}")
             k2, v2 = k.clone(), v.clone()
             j = torch.arange(T)

@@ -405,12 +405,16 @@ struct WaveTile {
     return pair_max(fmaxf(m2a, m2b));
   }
 
-  // Lazy running-maximum update with a tile's row maximum (raw scores); nothing with QKN.
+  // Lazy running-maximum update with a tile's row maximum (raw scores); nothing with QKN. Only
+  // the rows whose maximum grew by more than the slack move it (the others keep m_run, so their
+  // factor is exactly 1): a row's arithmetic depends on its own scores alone, never on whether
+  // another row of the wave triggered a rescale.
   __device__ __forceinline__ void decide(float mx) {
     if constexpr (QKN) return;
     const float m_tile = mx * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
+    const bool need = m_tile > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? m_tile : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
       m_run = m_new;
       l_run0 *= alpha;
@@ -482,14 +486,11 @@ struct WaveTile {
 
   // One pipelined step with a next tile: the scores of both 32-key blocks of tile t+1 (K tile at
   // kbuf) go to the matrix cores while the vector ALUs exponentiate tile t's scores (cur), then
-  // P(t) V(t) (V tile at vbuf). The LDS reads are issued ahead of the products that use them:
-  // all K fragments first, then the transposing V reads spread over the score products, so no
-  // product waits on a read issued right before it. The instruction order is fixed with
-  // scheduling groups (one score product, then a share of the exponentials and V reads).
+  // P(t) V(t) (V tile at vbuf). All 24 LDS reads (K fragments, then the transposing V reads) are
+  // issued before the first product, so no product waits on a read issued right before it; the
+  // compiler interleaves the exponentials with the products.
   __device__ __forceinline__ void step_pipelined(const char* kbuf, const char* vbuf,
                                                  const f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    constexpr int NS = 2 * C::KSTEPS;       // score products
-    constexpr int NV = 2 * 2 * C::DB * 2;   // transposing V reads (two per P V product)
     bf16x8 kf[2][C::KSTEPS];
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
@@ -497,7 +498,6 @@ struct WaveTile {
       for (int kb = 0; kb < 2; ++kb)
         kf[kb][s] = *reinterpret_cast<const bf16x8*>(kbuf + 32 * kb * C::ROW_BYTES + k_row_off +
                                                      16 * ((2 * s + hi) ^ k_swz));
-    __builtin_amdgcn_sched_barrier(0);
     u32x2 vp[2][2][C::DB][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -512,6 +512,16 @@ struct WaveTile {
             vp[kb][tt][db][u] =
                 ds_read_tr16_b64(vbuf + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
           }
+    // Every read above is issued before the first product: an empty volatile statement with a
+    // memory clobber keeps the reads above it, and passing the Q fragments through it makes the
+    // score products wait for it. (The scheduling-barrier builtins carry no memory dependence, so
+    // they do not order these reads; without this point each read lands right before its product
+    // and waits its full latency.)
+    if constexpr (C::KSTEPS == 4)
+      asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]) : : "memory");
+    else
+      asm volatile("" : "+v"(qf[0]), "+v"(qf[1]) : : "memory");
+    static_assert(C::KSTEPS == 4 || C::KSTEPS == 2, "the ordering point names every Q fragment");
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
@@ -520,14 +530,6 @@ struct WaveTile {
                                                           s == 0 ? f32x16{} : nxt[kb], 0, 0, 0);
     bf16x8 pf[2][2];
     exps(cur, pf);
-    // Order: per score product, its share of the V reads and of the vector work.
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, NV / NS, 0);     // V reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 64 / NS, 0);     // vector ALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -802,9 +804,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       // fully visible; tile t's blocks that the wave does not see hold -inf scores (zero
       // weights), so its exponentials and P V need no guards.
       if constexpr (has_next) {
-        // d = 64: LDS reads issued ahead of the products (scheduling groups); d = 32, where the
-        // step has half the products for the same exponentials, measures faster with the
-        // compiler's own order of the three parts.
+        // d = 64: every LDS read issued ahead of the products; d = 32, where the step has half
+        // the products for the same exponentials, measures faster with the compiler's own order
+        // of the three parts.
         if constexpr (D >= 64) {
           w.step_pipelined(kn, vc, cur, nxt);
         } else {
