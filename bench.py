@@ -34,6 +34,9 @@ Extra modes (used to collect rocprofv3 counters; they print no JSON):
                          single key split per head suffices; bwd: attn_bwd_ex's kernels, after
                          the two-call forward it reads), --steps times per layer
   --copy-calibration     run a plain 256 MiB device copy (known bytes) for counter scaling
+  --dma-calibration      run the attention kernel where it reads every byte once (non-causal,
+                         T = 128: one query block per head, each K/V tile read by one item), so
+                         the counters of its direct-to-LDS loads can be checked against known bytes
 """
 
 from __future__ import annotations
@@ -198,6 +201,7 @@ def main() -> int:
     ap.add_argument("--only", default=None,
                     choices=["attn", "kprologue", "attn_unfused", "prologue", "decode", "bwd"])
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--dma-calibration", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -214,7 +218,7 @@ def main() -> int:
     # The CPU baseline runs first, before anything touches the GPU, because its process pool
     # forks. Its inputs are the same seeded tensors the GPU step uses.
     cpu_result = None
-    if not (args.no_cpu_baseline or args.only or args.copy_calibration):
+    if not (args.no_cpu_baseline or args.only or args.copy_calibration or args.dma_calibration):
         names0 = [x.name for x in inputs.WORKLOADS] + [inputs.MODEL_DEFAULT.name]
         if args.workload in names0:
             import oracle
@@ -241,6 +245,25 @@ def main() -> int:
         torch.cuda.synchronize()
         print(f"copy calibration: {max(1, args.steps or 1)} copies of {n} bytes read + {n} bytes written",
               file=sys.stderr)
+        return 0
+
+    if args.dma_calibration:
+        # 4096 heads of 128 rows, d = 64, non-causal: each head is one item whose two K/V tiles
+        # and Q block the attention kernel loads once, directly into LDS.
+        Bc, Hc, Tc, dc = 64, 64, 128, 64
+        xs = [inputs.make_random((Bc, Hc, Tc, dc), torch.bfloat16, 90 + i).cuda() for i in range(3)]
+        kn_c = torch.empty_like(xs[1])
+        oc, lc = torch.empty_like(xs[0]), torch.empty((Bc, Hc, Tc), dtype=torch.float32, device="cuda")
+        cos_c, sin_c = ops.rope_table(Tc, dc)
+        ops.qknorm_rope(None, xs[1], cos_c, sin_c, k_out=kn_c)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps or 1)):
+            ops.attn_fwd_qnorm(xs[0], kn_c, xs[2], cos_c, sin_c, causal=False, out=oc, lse=lc)
+        torch.cuda.synchronize()
+        rd = 3 * xs[0].numel() * 2 + 2 * cos_c.numel() * 4
+        wr = oc.numel() * 2 + lc.numel() * 4
+        print(f"dma calibration: {max(1, args.steps or 1)} launches of attn_fwd_bf16_stream<64, "
+              f"non-causal>, each reading {rd} bytes and writing {wr} bytes", file=sys.stderr)
         return 0
 
     names = [w.name for w in inputs.WORKLOADS] + [inputs.MODEL_DEFAULT.name]
