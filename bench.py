@@ -8,7 +8,9 @@ QK-RMSNorm + RoPE of that layer's raw q and k and the attention forward with tha
 window, through the library's one-call layer entry point (attn_fwd_qknorm: a k-only
 norm + rotation kernel, then the attention kernel that normalises and rotates q as it loads
 it). Inputs are resident in HBM before timing starts; every layer has its own buffers. The
-two-call path (attn_qknorm_rope on q and k, then attn_fwd) is timed too and reported beside it.
+two-call path (attn_qknorm_rope on q and k, then attn_fwd) is timed too and reported beside it,
+and so is the layer in one launch ("k_in_kernel": attn_fwd_qknorm_ex with k_work NULL, the keys
+normalised and rotated inside the attention kernel; d <= 64).
 
 The value is counted the way the metric names it: TFLOP/s of unmasked attention work
 (4 d FLOPs per visible (query, key) pair) over the whole step's time, prologue included.
@@ -514,13 +516,30 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_ms = sum(a_.elapsed_time(b_) for a_, b_ in copy_ev) / args.steps
     del copy_src, copy_dst
-    # The two-call path, for comparison.
+    def nothing_step(l):
+        return 0
+
+    # The two-call path, and the layer in one launch with the keys normalised in the attention
+    # kernel (attn_fwd_qknorm_ex with k_work NULL, d <= 64), for comparison.
+    kin_ms = None
     if not args.no_cache_states:
         ms_per_step_unfused = time_steps(step_unfused)
         pro_ms, attn_unf_ms = time_launches(prologue, attention_unfused)
+        if d <= 64:
+            def layer_kin(l):
+                pq, pk, pv, _, _, po, pl = P[l]
+                return lib.attn_fwd_qknorm_ex(pq, pk, pv, None, po, pl, pcos, psin, B, H, H, T, d,
+                                              lay, eps, windows[l], 1, bf16, stream)
 
-    def nothing_step(l):
-        return 0
+            for l in range(L):
+                _lib.check("layer_kin", layer_kin(l))
+
+            def step_kin():
+                for l in range(L):
+                    layer_kin(l)
+
+            ms_per_step_kin = time_steps(step_kin)
+            kin_ms, _ = time_launches(layer_kin, nothing_step)
 
     # Decode (context): one generation step against each layer's keys and values as the cache.
     dec_ms = None
@@ -658,6 +677,16 @@ def main() -> int:
             "prologue_avg_launch_us": round(1e3 * sum(pro_ms) / L, 3),
             "prologue_bytes_per_launch": pro_bytes,
             "prologue_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
+        }
+    if kin_ms is not None:
+        result["k_in_kernel"] = {
+            "note": "the layer in one launch: attn_fwd_qknorm_ex with k_work NULL normalises and "
+                    "rotates each key tile inside the attention kernel (no k pass, no normalised "
+                    "k written); the step value uses the two-launch layer, which is faster here",
+            "ms_per_step": round(ms_per_step_kin, 5),
+            "value": round(step_flops / (ms_per_step_kin * 1e-3) / 1e12, 3),
+            "avg_launch_us": round(1e3 * sum(kin_ms) / L, 3),
+            "launch_us": [round(1e3 * t, 3) for t in kin_ms],
         }
     if dec_ms is not None:
         result["decode"] = {

@@ -173,14 +173,20 @@ int attn_fwd_qnorm(const void* q, const void* k, const void* v, void* out, float
  *   q, k, v          DEVICE [B][H][T][d] bf16, read (q and k before norm and rotation)
  *   k_work           DEVICE [B][H][T][d] bf16, written with RoPE(RMSNorm(k)) (the caller may
  *                    keep it, e.g. as the layer's keys); may equal k (normalised in place);
- *                    any other overlap with q, k, v, out or lse is ATTN_ERR_ALIAS
+ *                    any other overlap with q, k, v, out or lse is ATTN_ERR_ALIAS.
+ *                    NULL (d in {32, 64} only, else ATTN_ERR_NULL): the layer runs as one
+ *                    launch that RMS-normalises and rotates each key tile in on-chip memory as
+ *                    it streams in, and the normalised k is written nowhere
  *   out, lse         as in attn_fwd; out must not overlap q, k, v or k_work
  *   cos_tab, sin_tab DEVICE fp32 [T][d/2] from attn_rope_table
  *   eps              >= 0 and finite, as in attn_qknorm_rope
  *   window, causal   as in attn_fwd
  *   d in {32, 64, 128}; dtype must be ATTN_BF16 (else ATTN_ERR_DTYPE)
  * Rounding differs from attn_qknorm_rope + attn_fwd in one place: q's normalised, rotated row is
- * multiplied by log2(e)/sqrt(d) in fp32 before its one rounding to bf16.
+ * multiplied by log2(e)/sqrt(d) in fp32 before its one rounding to bf16. With k_work NULL the
+ * keys' rotation angles are also formed in the kernel in fp32 (t times the frequency that row 1
+ * of the tables gives, reduced to one turn), which moves a rotated key by up to about 2e-4 of its
+ * norm against the table's angles for T below 8192.
  */
 int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, void* out,
                     float* lse, const float* cos_tab, const float* sin_tab, int B, int H, int T,

@@ -196,7 +196,11 @@ def fused_args(**kw):
 
 FUSED_CASES = [
     ("null q", dict(q=None), _lib.ATTN_ERR_NULL),
-    ("null k_work", dict(kw=None), _lib.ATTN_ERR_NULL),
+    # k_work NULL: the keys are normalised in the attention kernel (d <= 64 only)
+    ("null k_work at d=128", dict(kw=None, d=128), _lib.ATTN_ERR_NULL),
+    ("null k_work at d=64 reaches the eps rule", dict(kw=None, eps=-1.0), _lib.ATTN_ERR_ARG),
+    ("null k_work at d=32 reaches the alias rule", dict(kw=None, d=32, out=Bp),
+     _lib.ATTN_ERR_ALIAS),
     ("null cos", dict(cos=None), _lib.ATTN_ERR_NULL),
     ("f32", dict(dtype=_lib.ATTN_F32), _lib.ATTN_ERR_DTYPE),
     ("dtype 3", dict(dtype=3), _lib.ATTN_ERR_DTYPE),

@@ -327,3 +327,94 @@ def test_fused_long_single_head_sampled(window):
     for h in range(H):
         sl = (slice(0, 1), slice(h, h + 1))
         check(out[sl], lse[sl], q[sl], k[sl], v[sl], window, rows=rows)
+
+
+# The layer in one launch (k_work NULL, write_k=False): keys normalised and rotated inside the
+# attention kernel, d 32 and 64. Same oracle and tolerances; the rotation angles of the keys are
+# formed in fp32 in the kernel instead of read from the fp64-built table.
+KIN_CASES = []
+for d in (32, 64):
+    KIN_CASES += [(d, 1, 1, 1, -1, 1), (d, 1, 2, 63, 1, 1), (d, 2, 1, 130, 0, 1),
+                  (d, 1, 3, 257, 100, 1), (d, 1, 2, 300, -1, 0), (d, 2, 2, 384, -1, 1),
+                  (d, 1, 1, 200, 199, 1), (d, 1, 2, 700, 333, 1)]
+KIN_CASES += [(64, 40, 16, 256, 128, 1), (32, 64, 12, 200, -1, 1)]
+
+
+@pytest.mark.parametrize("d,B,H,T,window,causal", KIN_CASES,
+                         ids=[f"d{c[0]}-B{c[1]}H{c[2]}T{c[3]}-W{c[4]}-c{c[5]}" for c in KIN_CASES])
+def test_k_in_kernel_parity(d, B, H, T, window, causal):
+    say(f"k in kernel parity d={d} B={B} H={H} T={T} W={window} causal={causal}")
+    q, k, v = (inputs.make_random((B, H, T, d), torch.bfloat16, s) for s in (151, 152, 153))
+    cos, sin = ops.rope_table(T, d)
+    out, lse, kw = ops.attn_fwd_qknorm(dev(q), dev(k), dev(v), cos, sin, window=window,
+                                       causal=bool(causal), write_k=False)
+    torch.cuda.synchronize()
+    assert kw is None
+    out, lse = out.cpu(), lse.cpu()
+    if B * H * T > 20000:
+        rows = np.unique(np.r_[0, 1, T // 2, T - 1, np.arange(0, T, 37)])
+        for sl in ((slice(0, 1), slice(0, 1)), (slice(B - 1, B), slice(H - 1, H))):
+            check(out[sl], lse[sl], q[sl], k[sl], v[sl], window, bool(causal), rows=rows)
+    else:
+        check(out, lse, q, k, v, window, bool(causal))
+
+
+@pytest.mark.parametrize("index", [i for i, w in enumerate(inputs.WORKLOADS)
+                                   if w.dtype == "bf16" and w.d <= 64],
+                         ids=[w.name for w in inputs.WORKLOADS if w.dtype == "bf16" and w.d <= 64])
+def test_k_in_kernel_full_size_sampled(index):
+    """Every layer at the workload's real shape with the keys normalised in the kernel; sampled
+    rows of sampled heads against the oracle, and every output within the bf16 budget of the
+    two-launch layer."""
+    w = inputs.WORKLOADS[index]
+    rng = np.random.default_rng(200 + index)
+    cos, sin = ops.rope_table(w.T, w.d)
+    for layer, window in enumerate(ops.sssl_windows(w.T, w.n_layer, w.pattern)):
+        say(f"k in kernel full {w.name} B={w.B} H={w.H} T={w.T} d={w.d} layer={layer} "
+            f"W={window}")
+        q, k, v = inputs.make_qkv(index, layer)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out, lse, _ = ops.attn_fwd_qknorm(qd, kd, vd, cos, sin, window=window, write_k=False)
+        o2, l2, _ = ops.attn_fwd_qknorm(qd, kd, vd, cos, sin, window=window)
+        torch.cuda.synchronize()
+        assert float((out.float() - o2.float()).abs().max()) <= BF16_TOL
+        assert float((lse - l2).abs().max()) <= LSE_TOL
+        del qd, kd, vd, o2, l2
+        heads = [(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))]
+        fixed = {0, 1, w.T - 1, w.T // 2, min(w.T - 1, window), min(w.T - 1, window + 1)}
+        rows = np.array(sorted(fixed | set(int(x) for x in rng.choice(w.T, 40, replace=False))))
+        for b, h in heads:
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            check(out[sl].cpu(), lse[sl].cpu(), q[sl], k[sl], v[sl], window, rows=rows)
+        del out, lse
+
+
+def test_k_in_kernel_gqa_and_bthd():
+    """Grouped-query heads and the [B][T][H][d] order with the keys normalised in the kernel."""
+    B, H, H_kv, T, d = 2, 6, 2, 290, 64
+    say("k in kernel GQA bthd")
+    q = inputs.make_random((B, H, T, d), torch.bfloat16, 161)
+    k, v = (inputs.make_random((B, H_kv, T, d), torch.bfloat16, s) for s in (162, 163))
+    cos, sin = ops.rope_table(T, d)
+    for layout in ("bhtd", "bthd"):
+        conv = (lambda x: dev(x.transpose(1, 2))) if layout == "bthd" else dev
+        out, lse, _ = ops.attn_fwd_qknorm(conv(q), conv(k), conv(v), cos, sin, window=90,
+                                          layout=layout, write_k=False)
+        o2, l2, _ = ops.attn_fwd_qknorm(conv(q), conv(k), conv(v), cos, sin, window=90,
+                                        layout=layout)
+        torch.cuda.synchronize()
+        assert float((out.float() - o2.float()).abs().max()) <= BF16_TOL
+        assert float((lse - l2).abs().max()) <= LSE_TOL
+        if layout == "bthd":
+            out = out.transpose(1, 2)
+        kx = k.repeat_interleave(H // H_kv, dim=1)
+        vx = v.repeat_interleave(H // H_kv, dim=1)
+        check(out.cpu(), lse.cpu(), q, kx, vx, 90)
+
+
+def test_k_in_kernel_needs_d_at_most_64():
+    B, H, T, d = 1, 1, 64, 128
+    q, k, v = (dev(inputs.make_random((B, H, T, d), torch.bfloat16, s)) for s in (1, 2, 3))
+    cos, sin = ops.rope_table(T, d)
+    with pytest.raises(RuntimeError):
+        ops.attn_fwd_qknorm(q, k, v, cos, sin, write_k=False)

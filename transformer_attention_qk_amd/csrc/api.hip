@@ -257,9 +257,18 @@ int attn_fwd_qknorm_ex(const void* q, const void* k, const void* v, void* k_work
                        float* lse, const float* cos_tab, const float* sin_tab, int B, int H,
                        int H_kv, int T, int d, int layout, float eps, int window, int causal,
                        int dtype, void* stream) {
-  if (!k_work) return ATTN_ERR_NULL;
   attn::Dims dm;
   int64_t n_q = 0, n_kv = 0;
+  if (!k_work) {
+    // k normalised and rotated inside the attention kernel, not written (d <= 64)
+    if (int rc = check_qnorm_args(q, k, v, out, lse, cos_tab, sin_tab, B, H, H_kv, T, d, layout,
+                                  eps, window, causal, dtype, &dm, &n_q, &n_kv))
+      return rc;
+    if (d > 64) return ATTN_ERR_NULL;
+    const hipError_t e = attn::launch_attn_fwd_bf16_qknorm_kin(
+        q, k, v, out, lse, cos_tab, sin_tab, eps, dm, window, causal, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
   if (int rc = check_qnorm_args(q, k_work, v, out, lse, cos_tab, sin_tab, B, H, H_kv, T, d,
                                 layout, eps, window, causal, dtype, &dm, &n_q, &n_kv))
     return rc;

@@ -606,14 +606,23 @@ __device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, i
 
 // ---------------------------------------------------------------------------------------------
 // Streaming kernel (d <= 64): persistent grid, direct-to-LDS K/V stream, pipelined tiles.
+//
+// KN (with QKN): K arrives raw, and each stream tile's 64 rows are RMS-normalised and rotated in
+// LDS, in place, once the tile has landed and before any wave reads it (the layer in one launch:
+// no separate k pass, no normalised k written). A tile is normalised by every item that streams
+// it. The rotation angles are formed in the kernel: the lane's frequencies w_j (radians per
+// position) come from row 1 of the rotation tables as atan2(sin w_j, cos w_j), and the angle of
+// position t is t w_j reduced to one turn in fp32 before __sinf / __cosf, so the rotated rows
+// differ from the k pass's (fp64 table) by the fp32 error of t w_j (below 2e-4 rad for t < 2^13).
 // ---------------------------------------------------------------------------------------------
-template <int D, int MODE, bool QKN>
+template <int D, int MODE, bool QKN, bool KN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
     const float* __restrict__ sin_tab, float eps, Geometry geo, FastDiv fd_bh, int T,
     int window_arg, float scale_log2, int nqt) {
   using C = FwdCfg<D>;
+  static_assert(!KN || QKN, "keys are normalised in the kernel only beside q");
   const int BH = (int)fd_bh.d;  // heads B * H; items are (head, query block) pairs
   const int window = (MODE == kCausalWindow) ? window_arg : -1;
   __shared__ __attribute__((aligned(16))) char smem[C::STREAM_LDS];
@@ -628,6 +637,118 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   const int q_slab = T * q_rs, kv_slab = T * kv_rs;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   const char* qbuf = smem + C::NSTAGE * 2 * C::TILE_BYTES;
+
+  // (KN) Each wave normalises rows 16 w .. 16 w + 15 of a K tile, four lanes per row; lane
+  // quarter p = lane % 4 holds chunk p of the row (columns 8 p .. 8 p + 7) and, at d = 64, chunk
+  // p + 4 (their rotation partners, d/2 further); at d = 32 the partner chunk p ^ 2 sits in lane
+  // p ^ 2. kfr[i]: turns per position of the lane's frequency index 8 (p % (CH / 2)) + i.
+  constexpr int KCH = C::CH;  // 16-byte chunks per row
+  float kfr[8];
+  if constexpr (KN) {
+    const int p = w.lane & 3;
+    const int j0 = 8 * (p % (KCH / 2));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float c1 = T > 1 ? cos_tab[D / 2 + j0 + i] : 1.f;
+      const float s1 = T > 1 ? sin_tab[D / 2 + j0 + i] : 0.f;
+      kfr[i] = atan2f(s1, c1) * 0.15915494309189535f;  // 1 / (2 pi)
+    }
+    // formed before the first direct load is issued, so their wait waits for nothing else
+    asm volatile("" : "+v"(kfr[0]), "+v"(kfr[1]), "+v"(kfr[2]), "+v"(kfr[3]), "+v"(kfr[4]),
+                 "+v"(kfr[5]), "+v"(kfr[6]), "+v"(kfr[7]) : : "memory");
+  }
+  // RMSNorm (weightless, eps) and the half-split rotation of the raw K tile in stage st, whose
+  // first key is at position t0: y_j = x_j cos + x_{j+d/2} sin, y_{j+d/2} = x_{j+d/2} cos - x_j sin
+  // with x = the row over its RMS, in fp32 with one rounding to bf16 (the k pass's arithmetic).
+  // Rows past T stay as loaded (zero).
+  auto norm_k_tile = [&](unsigned st, int t0) {
+    const int ln = w.lane;
+    const int r = 16 * w.wave + (ln >> 2), p = ln & 3;
+    const int sw = swz_k<D>(r);
+    char* row = smem + st * (2 * C::TILE_BYTES) + r * C::ROW_BYTES;
+    const float tpos = (float)(t0 + r);
+    float cs[8], sn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float turns = tpos * kfr[i];
+      turns -= rintf(turns);
+      const float th = turns * 6.283185307179586f;
+      cs[i] = __cosf(th);
+      sn[i] = __sinf(th);
+    }
+    if constexpr (KCH == 8) {  // d = 64: both halves of the pair in this lane
+      u32x4* pa = reinterpret_cast<u32x4*>(row + 16 * (p ^ sw));
+      u32x4* pb = reinterpret_cast<u32x4*>(row + 16 * ((p + 4) ^ sw));
+      const u32x4 wa = *pa, wb = *pb;
+      float a[8], b[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] = bf16lo_to_f32(wa[e]);
+        a[2 * e + 1] = bf16hi_to_f32(wa[e]);
+        b[2 * e] = bf16lo_to_f32(wb[e]);
+        b[2 * e + 1] = bf16hi_to_f32(wb[e]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(a[i], a[i], fmaf(b[i], b[i], ss));
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+      u32x4 ya, yb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * e + u;
+          const float xa = a[i] * rinv, xb = b[i] * rinv;
+          y1[u] = fmaf(xa, cs[i], xb * sn[i]);
+          y2[u] = fmaf(xb, cs[i], -(xa * sn[i]));
+        }
+        ya[e] = pack_bf16x2(y1[0], y1[1]);
+        yb[e] = pack_bf16x2(y2[0], y2[1]);
+      }
+      if (t0 + r < T) {
+        *pa = ya;
+        *pb = yb;
+      }
+    } else {  // d = 32: the partner chunk is in lane ^ 2
+      static_assert(KCH == 4, "K normalisation in the kernel covers d = 32 and d = 64");
+      u32x4* pa = reinterpret_cast<u32x4*>(row + 16 * (p ^ sw));
+      const u32x4 wa = *pa;
+      u32x4 wb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wb[e] = (uint32_t)__shfl_xor((int)wa[e], 2);
+      float a[8], b[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] = bf16lo_to_f32(wa[e]);
+        a[2 * e + 1] = bf16hi_to_f32(wa[e]);
+        b[2 * e] = bf16lo_to_f32(wb[e]);
+        b[2 * e + 1] = bf16hi_to_f32(wb[e]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(a[i], a[i], ss);
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+      const bool first = p < 2;
+      u32x4 ya;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * e + u;
+          const float xa = a[i] * rinv, xb = b[i] * rinv;
+          y[u] = first ? fmaf(xa, cs[i], xb * sn[i]) : fmaf(xa, cs[i], -(xb * sn[i]));
+        }
+        ya[e] = pack_bf16x2(y[0], y[1]);
+      }
+      if (t0 + r < T) *pa = ya;
+    }
+  };
 
   // Items of this workgroup: heaviest-first ranks dealt out in snake order. Workgroup g runs on
   // XCD g mod 8 (round-robin dispatch), and rank r = qb * BH + bh sits at position r mod P of its
@@ -695,6 +816,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   // (and so the waits) the same.
   int pk = 0, pt = 0, pte = 0;
   bool pvalid = true;
+  // (KN) first key positions of the two most recently issued tiles (-1: no tile)
+  int kpos_prev = -1, kpos_cur = -1;
   u32x4 prk, prv;
   unsigned st_issue = 0;
   auto seek = [&](int rank) {
@@ -709,6 +832,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const uint32_t kb_ = lds0 + st_issue * (2 * C::TILE_BYTES) + w.wave * (C::LPT * 1024);
     const uint32_t vb_ = kb_ + C::TILE_BYTES;
     const uint32_t base = pvalid ? (uint32_t)(pt * C::BN * kv_rs) : kOutOfRange;
+    if constexpr (KN) {
+      kpos_prev = kpos_cur;
+      kpos_cur = pvalid ? pt * C::BN : -1;
+    }
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
       dma16(prk, kb_ + u * 1024, base + kofs[u]);
@@ -736,6 +863,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   issue_next();
   wait_vmcnt<C::DMA_PER_TILE>();
   __syncthreads();
+  // (KN) tile 0 in place; the barrier after the Q fragments orders it before the first scores
+  if constexpr (KN) norm_k_tile(0, kpos_prev);
   typename WaveTile<D, MODE, QKN>::Rope rope;
   {
     w.rope_from_lds(smem + (C::NSTAGE - 1) * (2 * C::TILE_BYTES), rope);
@@ -769,6 +898,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       // landed (tile 2 may still be in flight) before any wave reads it.
       wait_vmcnt<C::DMA_PER_TILE>();
       __syncthreads();
+      if constexpr (KN) {
+        if (kpos_prev >= 0) norm_k_tile(1, kpos_prev);
+        __syncthreads();
+      }
     }
     const int rank_n = rank_of(k + 1);
     const bool more = rank_n < n_items;
@@ -827,6 +960,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       if (has_next) w.decide(mx);
       wait_vmcnt<(C::PREFETCH - 2) * C::DMA_PER_TILE>();  // the tile two stages ahead has landed
       __syncthreads();
+      if constexpr (KN) {
+        // (KN) that tile, issued one step before this step's, in place before its first read
+        if (kpos_prev >= 0) norm_k_tile((st_comp + 2) & (C::NSTAGE - 1), kpos_prev);
+        __syncthreads();
+      }
       st_comp = (st_comp + 1) & (C::NSTAGE - 1);
     };
     const std::true_type more_tiles;
@@ -999,7 +1137,7 @@ struct Bf16Args {
   Geometry geo;
 };
 
-template <int D, int MODE, bool QKN>
+template <int D, int MODE, bool QKN, bool KN = false>
 static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int nqt = (a.T + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
@@ -1008,14 +1146,15 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
   if constexpr (D <= 64) {
     int resident = 0;
     struct Tag {};
-    hipError_t e = resident_workgroups<Tag>(attn_fwd_bf16_stream<D, MODE, QKN>, &resident);
+    hipError_t e = resident_workgroups<Tag>(attn_fwd_bf16_stream<D, MODE, QKN, KN>, &resident);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
-    hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN, KN>), dim3(grid), dim3(256), 0, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse,
                        a.cos_tab, a.sin_tab, a.eps, a.geo, make_fastdiv((uint32_t)BH), a.T,
                        a.window, scale_log2, nqt);
   } else {
+    static_assert(!KN, "keys are normalised in the kernel only by the streaming kernel (d <= 64)");
     hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE, QKN>), dim3((unsigned)n_items), dim3(256), 0,
                        stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out,
                        a.lse, a.cos_tab, a.sin_tab, a.eps, a.geo, BH, a.T, a.window, scale_log2, nqt,
@@ -1024,18 +1163,18 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool QKN>
+template <int D, bool QKN, bool KN = false>
 static hipError_t launch_bf16_d(Bf16Args a, int causal, hipStream_t stream) {
   // A window of T - 1 or more hides nothing: run it as plain causal.
   if (!causal) {
     a.window = -1;
-    return launch_bf16_t<D, kNonCausal, QKN>(a, stream);
+    return launch_bf16_t<D, kNonCausal, QKN, KN>(a, stream);
   }
   if (a.window < 0 || a.window >= a.T - 1) {
     a.window = -1;
-    return launch_bf16_t<D, kCausal, QKN>(a, stream);
+    return launch_bf16_t<D, kCausal, QKN, KN>(a, stream);
   }
-  return launch_bf16_t<D, kCausalWindow, QKN>(a, stream);
+  return launch_bf16_t<D, kCausalWindow, QKN, KN>(a, stream);
 }
 
 template <bool QKN>
@@ -1060,6 +1199,17 @@ hipError_t launch_attn_fwd_bf16_qknorm(const void* q, const void* k, const void*
   const Bf16Args a{q, k, v, out, lse, cos_tab, sin_tab, eps, dm.B, dm.H, dm.T, window,
                    make_geometry(dm)};
   return launch_bf16<true>(a, dm.d, causal, stream);
+}
+
+hipError_t launch_attn_fwd_bf16_qknorm_kin(const void* q, const void* k, const void* v, void* out,
+                                           float* lse, const float* cos_tab,
+                                           const float* sin_tab, float eps, const Dims& dm,
+                                           int window, int causal, hipStream_t stream) {
+  const Bf16Args a{q, k, v, out, lse, cos_tab, sin_tab, eps, dm.B, dm.H, dm.T, window,
+                   make_geometry(dm)};
+  if (dm.d == 32) return launch_bf16_d<32, true, true>(a, causal, stream);
+  if (dm.d == 64) return launch_bf16_d<64, true, true>(a, causal, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attn

@@ -89,6 +89,13 @@ hipError_t launch_attn_fwd_bf16_qknorm(const void* q, const void* k, const void*
                                        float eps, const Dims& dm, int window, int causal,
                                        hipStream_t stream);
 
+// The same with raw k: each K tile is RMS-normalised and rotated inside the kernel, in LDS, and
+// the normalised k is not written. d in {32, 64}.
+hipError_t launch_attn_fwd_bf16_qknorm_kin(const void* q, const void* k, const void* v, void* out,
+                                           float* lse, const float* cos_tab,
+                                           const float* sin_tab, float eps, const Dims& dm,
+                                           int window, int causal, hipStream_t stream);
+
 // fp32 attention. d in {16, 32, 64, 128}.
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
                                float* lse, const Dims& dm, int window, int causal,

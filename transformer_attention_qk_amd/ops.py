@@ -175,10 +175,12 @@ def attn_fwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torc
                     sin: torch.Tensor, window: int = -1, causal: bool = True, eps: float = 1e-6,
                     k_work: torch.Tensor | None = None, out: torch.Tensor | None = None,
                     lse: torch.Tensor | None = None, want_lse: bool = True,
-                    layout: str = "bhtd"):
+                    layout: str = "bhtd", write_k: bool = True):
     """QK-norm + RoPE of raw bf16 q, k and attention in one library call. Shapes as in attn_fwd.
 
-    Returns (out, lse, k_work); k_work holds RoPE(RMSNorm(k)) (it may be ``k`` itself).
+    Returns (out, lse, k_work); k_work holds RoPE(RMSNorm(k)) (it may be ``k`` itself). With
+    write_k False (d 32 or 64) the keys are normalised inside the attention kernel, nothing is
+    written for them and k_work is returned as None.
     """
     lib = _lib.load()
     _require(q, "q", dtype=torch.bfloat16)
@@ -186,8 +188,11 @@ def attn_fwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cos: torc
     B, H, H_kv, T, d = _geometry(q, k, layout)
     _require(v, "v", k.shape, q.dtype)
     _rope_tables(cos, sin, T, d)
-    k_work = torch.empty_like(k) if k_work is None else k_work
-    _require(k_work, "k_work", k.shape, q.dtype)
+    if write_k:
+        k_work = torch.empty_like(k) if k_work is None else k_work
+        _require(k_work, "k_work", k.shape, q.dtype)
+    elif k_work is not None:
+        raise ValueError("k_work is not written when write_k is False")
     out = torch.empty_like(q) if out is None else out
     _require(out, "out", q.shape, q.dtype)
     lse = _lse(lse, want_lse, B, H, T, q.device)
