@@ -682,7 +682,8 @@ def main() -> int:
         result["k_in_kernel"] = {
             "note": "the layer in one launch: attn_fwd_qknorm_ex with k_work NULL normalises and "
                     "rotates each key tile inside the attention kernel (no k pass, no normalised "
-                    "k written); the step value uses the two-launch layer, which is faster here",
+                    "k written); the step value uses the two-launch layer (the default, which "
+                    "also returns the normalised k)",
             "ms_per_step": round(ms_per_step_kin, 5),
             "value": round(step_flops / (ms_per_step_kin * 1e-3) / 1e12, 3),
             "avg_launch_us": round(1e3 * sum(kin_ms) / L, 3),

@@ -613,7 +613,8 @@ __device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, i
 // it. The rotation angles are formed in the kernel: the lane's frequencies w_j (radians per
 // position) come from row 1 of the rotation tables as atan2(sin w_j, cos w_j), and the angle of
 // position t is t w_j reduced to one turn in fp32 before __sinf / __cosf, so the rotated rows
-// differ from the k pass's (fp64 table) by the fp32 error of t w_j (below 2e-4 rad for t < 2^13).
+// differ from the k pass's (fp64 table) by the fp32 error of t w_j (below 2e-4 rad for t < 2^13);
+// the row's RMS uses v_rsq_f32 (about 1 ulp) where the k pass divides by a square root.
 // ---------------------------------------------------------------------------------------------
 template <int D, int MODE, bool QKN, bool KN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
@@ -638,13 +639,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   const char* qbuf = smem + C::NSTAGE * 2 * C::TILE_BYTES;
 
-  // (KN) Each wave normalises rows 16 w .. 16 w + 15 of a K tile, four lanes per row; lane
+  // (KN) Each wave normalises rows 16 w .. 16 w + 15 of a K tile -- the rows its own direct
+  // loads brought in, so its own s_waitcnt covers them and the barrier that follows (the one
+  // that publishes the landed tile) publishes the normalised rows too -- four lanes per row; lane
   // quarter p = lane % 4 holds chunk p of the row (columns 8 p .. 8 p + 7) and, at d = 64, chunk
   // p + 4 (their rotation partners, d/2 further); at d = 32 the partner chunk p ^ 2 sits in lane
   // p ^ 2. kfr[i]: turns per position of the lane's frequency index 8 (p % (CH / 2)) + i.
   constexpr int KCH = C::CH;  // 16-byte chunks per row
   float kfr[8];
   if constexpr (KN) {
+    static_assert(C::LPT * 64 / C::CH == 16, "a wave's direct loads of a K tile are its 16 rows");
     const int p = w.lane & 3;
     const int j0 = 8 * (p % (KCH / 2));
 #pragma unroll
@@ -670,12 +674,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     float cs[8], sn[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      // v_sin_f32 / v_cos_f32 take the angle in turns; reduced to [-1/2, 1/2] first
       float turns = tpos * kfr[i];
       turns -= rintf(turns);
-      const float th = turns * 6.283185307179586f;
-      cs[i] = __cosf(th);
-      sn[i] = __sinf(th);
+      cs[i] = __builtin_amdgcn_cosf(turns);
+      sn[i] = __builtin_amdgcn_sinf(turns);
     }
+    // sums over the row's four lanes (lanes 4 m .. 4 m + 3, a DPP quad)
+    auto quad_sum = [](float x) {
+      x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1,
+                                                                0xF, 0xF, false));  // lane ^ 1
+      x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E,
+                                                                0xF, 0xF, false));  // lane ^ 2
+      return x;
+    };
     if constexpr (KCH == 8) {  // d = 64: both halves of the pair in this lane
       u32x4* pa = reinterpret_cast<u32x4*>(row + 16 * (p ^ sw));
       u32x4* pb = reinterpret_cast<u32x4*>(row + 16 * ((p + 4) ^ sw));
@@ -691,9 +703,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(a[i], a[i], fmaf(b[i], b[i], ss));
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+      ss = quad_sum(ss);
+      // v_rsq_f32 (about 1 ulp) is ample: the row is rounded to bf16 right after
+      const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
       u32x4 ya, yb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -718,7 +730,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       const u32x4 wa = *pa;
       u32x4 wb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wb[e] = (uint32_t)__shfl_xor((int)wa[e], 2);
+      for (int e = 0; e < 4; ++e)  // lane ^ 2 (DPP quad permutation 2, 3, 0, 1)
+        wb[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)wa[e], 0x4E, 0xF, 0xF, false);
       float a[8], b[8];
       float ss = 0.f;
 #pragma unroll
@@ -730,9 +743,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(a[i], a[i], ss);
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+      ss = quad_sum(ss);
+      const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
       const bool first = p < 2;
       u32x4 ya;
 #pragma unroll
@@ -862,9 +874,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   issue_next();
   issue_next();
   wait_vmcnt<C::DMA_PER_TILE>();
-  __syncthreads();
-  // (KN) tile 0 in place; the barrier after the Q fragments orders it before the first scores
+  // (KN) the wave's rows of tile 0, in place, before the barrier publishes them
   if constexpr (KN) norm_k_tile(0, kpos_prev);
+  __syncthreads();
   typename WaveTile<D, MODE, QKN>::Rope rope;
   {
     w.rope_from_lds(smem + (C::NSTAGE - 1) * (2 * C::TILE_BYTES), rope);
@@ -897,11 +909,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       // The workgroup's first item: tile 1 of the stream, issued in the workgroup prologue, has
       // landed (tile 2 may still be in flight) before any wave reads it.
       wait_vmcnt<C::DMA_PER_TILE>();
-      __syncthreads();
       if constexpr (KN) {
         if (kpos_prev >= 0) norm_k_tile(1, kpos_prev);
-        __syncthreads();
       }
+      __syncthreads();
     }
     const int rank_n = rank_of(k + 1);
     const bool more = rank_n < n_items;
@@ -959,12 +970,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       }
       if (has_next) w.decide(mx);
       wait_vmcnt<(C::PREFETCH - 2) * C::DMA_PER_TILE>();  // the tile two stages ahead has landed
-      __syncthreads();
       if constexpr (KN) {
-        // (KN) that tile, issued one step before this step's, in place before its first read
+        // (KN) the wave's rows of that tile (issued one step before this step's), in place,
+        // before the barrier publishes them
         if (kpos_prev >= 0) norm_k_tile((st_comp + 2) & (C::NSTAGE - 1), kpos_prev);
-        __syncthreads();
       }
+      __syncthreads();
       st_comp = (st_comp + 1) & (C::NSTAGE - 1);
     };
     const std::true_type more_tiles;
