@@ -74,8 +74,8 @@ __device__ __forceinline__ void chunk_f32(u32x4 w, float (&x)[16 / sizeof(Elem)]
 
 // FINAL: one split per (batch, kv head) (n_split = 1); the workgroup writes out and lse itself
 // and the workspace is not touched.
-template <typename Elem, int D, bool FINAL>
-__global__ __launch_bounds__(256) void attn_decode_partial(
+template <typename Elem, int D, bool FINAL, int NW = kDecodeWaves>
+__global__ __launch_bounds__(64 * NW) void attn_decode_partial(
     const Elem* __restrict__ Qv, const Elem* __restrict__ K, const Elem* __restrict__ V,
     const int* __restrict__ lengths, float* __restrict__ ws, Elem* __restrict__ out,
     float* __restrict__ lse, Geometry geo, int H_kv, int S, int window, int n_split,
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_decode_partial(
   using C = DecCfg<Elem, D>;
   // Per query head (two heads alternate, so one barrier per head suffices): each wave's
   // unnormalised o[D], then its m and l.
-  __shared__ float red[2][kDecodeWaves][D + 2];
+  __shared__ float red[2][NW][D + 2];
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = (int)blockIdx.x % n_split;
   const int bg = (int)blockIdx.x / n_split;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void attn_decode_partial(
   const int per_split = (n - lo + n_split - 1) / n_split;
   const int s0 = lo + split * per_split;
   const int s1 = min(n, s0 + per_split);
-  const int per_wave = (per_split + kDecodeWaves - 1) / kDecodeWaves;
+  const int per_wave = (per_split + NW - 1) / NW;
   const int w0 = s0 + wave * per_wave;
   const int cnt = min(s1, w0 + per_wave) - w0;  // rows of this wave (wave-uniform; may be <= 0)
   // Workspace: unnormalised outputs [B][H][n_split][D], then m and l [B][H][n_split].
@@ -196,11 +196,11 @@ __global__ __launch_bounds__(256) void attn_decode_partial(
       float (*rp)[D + 2] = red[hh & 1];
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w)
+      for (int w = 0; w < NW; ++w)
         if (rp[w][D + 1] > 0.f) M = fmaxf(M, rp[w][D]);
       float L = 0.f, o = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float lw = rp[w][D + 1];
         if (lw > 0.f) {
           const float fw = __builtin_amdgcn_exp2f(rp[w][D] - M);
@@ -298,6 +298,25 @@ hipError_t decode_scratch(void** ptr) {
   return hipSuccess;
 }
 
+// Compute units of the current device (cached per device; threads that race on the first query
+// store the same value).
+static int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const bool slot = dev >= 0 && dev < kMaxDevices;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (slot && cus > 0) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 int decode_splits(int B, int H, int S, int d, int window) {
   const int keys = (window >= 0 && window + 1 < S) ? window + 1 : S;
   const int64_t by_keys = (keys + decode_split_keys(d) - 1) / decode_split_keys(d);
@@ -321,10 +340,25 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
   const int keys = (window >= 0 && window + 1 < dm.T) ? window + 1 : dm.T;
   if ((int64_t)dm.B * dm.H_kv * kDecodeWaves >= kDecodeSingleWaves &&
       keys <= kDecodeSingleBatches * decode_split_keys(D)) {
-    hipLaunchKernelGGL((attn_decode_partial<Elem, D, true>), dim3((unsigned)(dm.B * dm.H_kv)),
-                       dim3(256), 0, stream, (const Elem*)q, (const Elem*)k, (const Elem*)v,
-                       lengths, (float*)ws, (Elem*)out, lse, geo, dm.H_kv, dm.T, window, 1,
-                       (int64_t)dm.B * dm.H, scale_log2);
+    // bf16 with more than four batches and at most one workgroup per compute unit: eight waves
+    // instead of four (each with at most two batches), twice the loads in flight for the same
+    // workgroups. An eight-wave workgroup takes a whole compute unit's registers, so with more
+    // workgroups than compute units four waves keep them all resident at once. (Sixteen waves
+    // would cap the registers at 128 per lane, below what a wave's batch takes: it spills.)
+    const int batches = (keys + decode_wave_keys(D) - 1) / decode_wave_keys(D);
+    const dim3 grid((unsigned)(dm.B * dm.H_kv));
+#define ATTN_DEC_SINGLE(NWV)                                                                     \
+  hipLaunchKernelGGL((attn_decode_partial<Elem, D, true, NWV>), grid, dim3(64 * NWV), 0, stream, \
+                     (const Elem*)q, (const Elem*)k, (const Elem*)v, lengths, (float*)ws,        \
+                     (Elem*)out, lse, geo, dm.H_kv, dm.T, window, 1, (int64_t)dm.B * dm.H,       \
+                     scale_log2)
+    bool eight = false;
+    if constexpr (sizeof(Elem) == 2) {
+      eight = batches > 4 && (int64_t)dm.B * dm.H_kv <= device_cus();
+      if (eight) ATTN_DEC_SINGLE(8);
+    }
+    if (!eight) ATTN_DEC_SINGLE(4);
+#undef ATTN_DEC_SINGLE
     return hipGetLastError();
   }
   const int n_split = decode_splits(dm.B, dm.H, dm.T, D, window);
