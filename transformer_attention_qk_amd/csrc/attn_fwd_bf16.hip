@@ -486,9 +486,8 @@ struct WaveTile {
 
   // One pipelined step with a next tile: the scores of both 32-key blocks of tile t+1 (K tile at
   // kbuf) go to the matrix cores while the vector ALUs exponentiate tile t's scores (cur), then
-  // P(t) V(t) (V tile at vbuf). All 24 LDS reads (K fragments, then the transposing V reads) are
-  // issued before the first product, so no product waits on a read issued right before it; the
-  // compiler interleaves the exponentials with the products.
+  // P(t) V(t) (V tile at vbuf). The compiler places each LDS read near its product and
+  // interleaves the exponentials with the products.
   __device__ __forceinline__ void step_pipelined(const char* kbuf, const char* vbuf,
                                                  const f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     bf16x8 kf[2][C::KSTEPS];
@@ -512,16 +511,6 @@ struct WaveTile {
             vp[kb][tt][db][u] =
                 ds_read_tr16_b64(vbuf + row * C::ROW_BYTES + 16 * (c ^ v_swz) + 8 * (v_b & 1));
           }
-    // Every read above is issued before the first product: an empty volatile statement with a
-    // memory clobber keeps the reads above it, and passing the Q fragments through it makes the
-    // score products wait for it. (The scheduling-barrier builtins carry no memory dependence, so
-    // they do not order these reads; without this point each read lands right before its product
-    // and waits its full latency.)
-    if constexpr (C::KSTEPS == 4)
-      asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]) : : "memory");
-    else
-      asm volatile("" : "+v"(qf[0]), "+v"(qf[1]) : : "memory");
-    static_assert(C::KSTEPS == 4 || C::KSTEPS == 2, "the ordering point names every Q fragment");
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
@@ -948,9 +937,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       // fully visible; tile t's blocks that the wave does not see hold -inf scores (zero
       // weights), so its exponentials and P V need no guards.
       if constexpr (has_next) {
-        // d = 64: every LDS read issued ahead of the products; d = 32, where the step has half
-        // the products for the same exponentials, measures faster with the compiler's own order
-        // of the three parts.
+        // d = 64: the score products of t+1 and the P V products of t in one scheduling region;
+        // d = 32, where the step has half the products for the same exponentials, measures
+        // faster with the three parts in sequence.
         if constexpr (D >= 64) {
           w.step_pipelined(kn, vc, cur, nxt);
         } else {
