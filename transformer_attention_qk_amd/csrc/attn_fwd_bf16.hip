@@ -38,8 +38,7 @@
 //     boundaries. The next item's Q block arrives by the same route during the current item's
 //     last tile. Inside an item each wave runs a software pipeline: the scores of tile t+1 go to
 //     the matrix cores while the vector ALUs exponentiate tile t, then P(t) V(t) while the
-//     vector ALUs mask and reduce the scores of tile t+1, with an explicit MFMA / VALU
-//     interleave on unmasked tiles.
+//     vector ALUs mask and reduce the scores of tile t+1.
 //   - attn_fwd_bf16_tile (d = 128): one workgroup per item, K/V staged through registers one
 //     tile ahead. The pipelined form needs more registers than two waves per SIMD have at
 //     d = 128, where the matrix work per tile doubles while the softmax work stays the same.
