@@ -206,7 +206,8 @@ def sample_rows(T, window, rng):
                          ids=[w.name for w in inputs.WORKLOADS])
 def test_layer_parity_full_size_sampled(index):
     """Every layer of the workload at its real shape, launched as the bench launches it; the
-    oracle checks sampled rows of sampled heads."""
+    oracle checks sampled rows of sampled heads, and the outputs, which start as NaN, must all be
+    written (the kernel's item order reaches every (head, query block))."""
     w = inputs.WORKLOADS[index]
     wins = ops.sssl_windows(w.T, w.n_layer, w.pattern)
     rng = np.random.default_rng(index)
@@ -216,8 +217,11 @@ def test_layer_parity_full_size_sampled(index):
         q, k, v = inputs.make_qkv(index, layer)
         qd, kd, vd = dev(q), dev(k), dev(v)
         qn, kn = ops.qknorm_rope(qd, kd, cos, sin, 1e-6)
-        out, lse = ops.attn_fwd(qn, kn, vd, window=window)
+        out0 = torch.full(qd.shape, float("nan"), dtype=qd.dtype, device="cuda")
+        lse0 = torch.full((w.B, w.H, w.T), float("nan"), dtype=torch.float32, device="cuda")
+        out, lse = ops.attn_fwd(qn, kn, vd, window=window, out=out0, lse=lse0)
         torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
         heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H)))
                                                for _ in range(SAMPLE_HEADS - 2)]
         rows = sample_rows(w.T, window, rng)

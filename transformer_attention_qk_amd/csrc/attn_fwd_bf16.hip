@@ -47,8 +47,14 @@
 // unconditional.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
+#include <functional>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -581,7 +587,7 @@ struct WaveTile {
 
 // Key range [lo, up) of an item's query block and its tile range [tb, te).
 template <int D, int MODE>
-__device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, int& te) {
+__host__ __device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, int& te) {
   using C = FwdCfg<D>;
   int lo = 0, up = T;
   if constexpr (MODE != kNonCausal) {
@@ -591,6 +597,20 @@ __device__ __forceinline__ void item_tiles(int q0, int T, int window, int& tb, i
   tb = lo / C::BN;
   te = (up + C::BN - 1) / C::BN;
 }
+
+// Head-grouped item order of the streaming kernel (rounds = 0: the snake order). Round k gives
+// the workgroups of class c = g mod 8 the heads c + 8 (k per_round + j), j < per_round, all of
+// their nqt query blocks at once: workgroup i = g / 8 of the class takes head j = i / nqt and the
+// query block q(k nqt + i mod nqt) (rank order: 0 is the heaviest, the last block of the head),
+// byte e of the table, four to a word so that the kernel reads it with scalar loads (a vector
+// load would count among the tile loads the kernel waits for).
+constexpr int kOrderBytes = 256;
+struct ItemOrder {
+  int rounds;
+  int nqt;
+  int per_round;
+  unsigned q4[kOrderBytes / 4];
+};
 
 // ---------------------------------------------------------------------------------------------
 // Streaming kernel (d <= 64): persistent grid, direct-to-LDS K/V stream, pipelined tiles.
@@ -609,7 +629,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ cos_tab,
     const float* __restrict__ sin_tab, float eps, Geometry geo, FastDiv fd_bh, int T,
-    int window_arg, float scale_log2, int nqt) {
+    int window_arg, float scale_log2, int nqt, const ItemOrder ord) {
   using C = FwdCfg<D>;
   static_assert(!KN || QKN, "keys are normalised in the kernel only beside q");
   const int BH = (int)fd_bh.d;  // heads B * H; items are (head, query block) pairs
@@ -750,13 +770,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     }
   };
 
-  // Items of this workgroup: heaviest-first ranks dealt out in snake order. Workgroup g runs on
-  // XCD g mod 8 (round-robin dispatch), and rank r = qb * BH + bh sits at position r mod P of its
-  // round; when P is a multiple of 8 the odd rounds reverse the order within each class of
-  // workgroups g = c mod 8, so the position keeps its class and, when BH is a multiple of 8 too,
-  // every query block of a head runs on one XCD and its K/V tiles are cached in one L2.
+  // Items of this workgroup, as ranks r = qb * BH + bh in heaviest-first order (qb counts query
+  // blocks from the head's last one). Workgroup g runs on XCD g mod 8 (round-robin dispatch).
+  // Head-grouped order (ord.rounds > 0): the query blocks of a head all run in the same round on
+  // one XCD, so each K/V tile is read from its L2 by all of them at nearly the same time, and the
+  // per-round permutations of the blocks (chosen by the launcher) even out the workgroups' loads.
+  // Snake order otherwise: rank r sits at position r mod P of its round; when P is a multiple of
+  // 8 the odd rounds reverse the order within each class of workgroups g = c mod 8, so a head's
+  // query blocks still share an XCD when BH is a multiple of 8, but in different rounds.
   const int g_rev = ((P & 7) == 0) ? ((((P >> 3) - 1 - (g >> 3)) << 3) + (g & 7)) : (P - 1 - g);
-  auto rank_of = [&](int k) { return k * P + ((k & 1) ? g_rev : g); };
+  auto rank_of = [&](int k) {
+    if (ord.rounds > 0) {
+      if (k >= ord.rounds) return n_items;
+      const int i = g >> 3;
+      const int j = i / ord.nqt, s = i - j * ord.nqt;
+      const int e = k * ord.nqt + s;
+      const int q = (int)((ord.q4[e >> 2] >> (8 * (e & 3))) & 0xffu);
+      return q * BH + (g & 7) + 8 * (k * ord.per_round + j);
+    }
+    return k * P + ((k & 1) ? g_rev : g);
+  };
   auto decode = [&](int rank, int& bh, int& q0, int& tb, int& te) {
     const int qb = (int)fd_bh.div((uint32_t)rank);
     bh = rank - qb * BH;
@@ -1125,6 +1158,146 @@ static hipError_t resident_workgroups(Kern kern, int* out) {
   return hipSuccess;
 }
 
+// Per-round permutations sig[k] of the n query blocks over the n workgroups of a head's group
+// (block costs c, in tiles plus one for the transition, in rank order), so that the workgroups'
+// summed costs stay close to their mean. Rounds alternate the identity and the reverse (which
+// pairs heavy with light blocks); an odd count of three or more starts with the best triple
+// (sig 1 over every permutation when n <= 8, sig 2 by bottleneck matching); single swaps within
+// a round that lower the largest sum finish it. Returns the largest sum.
+static bool match_under(const std::vector<int>& base, const std::vector<int>& c, int cap,
+                        std::vector<int>& perm) {
+  const int n = (int)c.size();
+  std::vector<int> owner(n, -1);  // owner[q]: slot holding block q
+  std::vector<char> seen;
+  std::function<bool(int)> aug = [&](int s) {
+    for (int q = 0; q < n; ++q) {
+      if (base[s] + c[q] > cap || seen[q]) continue;
+      seen[q] = 1;
+      if (owner[q] < 0 || aug(owner[q])) {
+        owner[q] = s;
+        return true;
+      }
+    }
+    return false;
+  };
+  for (int s = 0; s < n; ++s) {
+    seen.assign(n, 0);
+    if (!aug(s)) return false;
+  }
+  perm.assign(n, 0);
+  for (int q = 0; q < n; ++q) perm[owner[q]] = q;
+  return true;
+}
+
+static int balance_rounds(const std::vector<int>& c, int R, std::vector<std::vector<int>>& sig) {
+  const int n = (int)c.size();
+  sig.assign(R, std::vector<int>(n));
+  for (int k = 0; k < R; ++k)
+    for (int q = 0; q < n; ++q) sig[k][q] = (k % 2 == 0) ? q : n - 1 - q;
+  if (R % 2 == 1 && R >= 3 && n >= 2 && n <= 8) {
+    // rounds 0..2: identity, the best sig 1, then sig 2 by bottleneck matching; the rest pairs
+    const int cmin = *std::min_element(c.begin(), c.end());
+    const int cmax = *std::max_element(c.begin(), c.end());
+    int csum = 0;
+    for (int x : c) csum += x;
+    int best = 3 * cmax + 1;
+    std::vector<int> s1(n), base(n), p2, best1, best2;
+    for (int q = 0; q < n; ++q) s1[q] = q;
+    do {
+      int bmax = 0;
+      for (int q = 0; q < n; ++q) {
+        base[q] = c[q] + c[s1[q]];
+        bmax = std::max(bmax, base[q]);
+      }
+      const int lb = std::max(bmax + cmin, (3 * csum + n - 1) / n);
+      for (int cap = lb; cap < best; ++cap) {
+        if (match_under(base, c, cap, p2)) {
+          best = cap;
+          best1 = s1;
+          best2 = p2;
+          break;
+        }
+      }
+    } while (std::next_permutation(s1.begin(), s1.end()));
+    if (!best1.empty()) {
+      sig[1] = best1;
+      sig[2] = best2;
+      for (int k = 3; k < R; ++k)
+        for (int q = 0; q < n; ++q) sig[k][q] = (k % 2 == 1) ? n - 1 - q : q;
+    }
+  }
+  std::vector<int> load(n, 0);
+  for (int k = 0; k < R; ++k)
+    for (int q = 0; q < n; ++q) load[q] += c[sig[k][q]];
+  for (int it = 0; it < 64 * n * R; ++it) {
+    const int sm = (int)(std::max_element(load.begin(), load.end()) - load.begin());
+    int bk = -1, bs = -1, bnew = load[sm];
+    for (int k = 0; k < R; ++k)
+      for (int s2 = 0; s2 < n; ++s2) {
+        if (s2 == sm) continue;
+        const int a = sig[k][sm], b = sig[k][s2];
+        const int m2 = std::max(load[sm] - c[a] + c[b], load[s2] - c[b] + c[a]);
+        if (m2 < bnew) {
+          bnew = m2;
+          bk = k;
+          bs = s2;
+        }
+      }
+    if (bk < 0) break;
+    const int a = sig[bk][sm], b = sig[bk][bs];
+    load[sm] += c[b] - c[a];
+    load[bs] += c[a] - c[b];
+    sig[bk][sm] = b;
+    sig[bk][bs] = a;
+  }
+  return *std::max_element(load.begin(), load.end());
+}
+
+// The head-grouped order for a launch of P workgroups, or rounds = 0 (the snake order) when the
+// shape does not divide into whole rounds, the table does not fit, or the best permutations found
+// leave a workgroup more than 8 % above the mean. Permutations are kept per (costs, rounds).
+template <int D, int MODE>
+static ItemOrder item_order(int P, int BH, int T, int window, int nqt) {
+  ItemOrder ord{};
+  if (P % 8 != 0 || BH % 8 != 0 || nqt < 1 || nqt > 255) return ord;
+  const int J = P / 8, hpc = BH / 8;
+  if (J % nqt != 0) return ord;
+  const int per_round = J / nqt;
+  if (hpc % per_round != 0) return ord;
+  const int R = hpc / per_round;
+  if ((int64_t)R * nqt > kOrderBytes) return ord;
+  std::vector<int> c(nqt);
+  int64_t total = 0;
+  for (int q = 0; q < nqt; ++q) {
+    int tb = 0, te = 0;
+    item_tiles<D, MODE>((nqt - 1 - q) * FwdCfg<D>::BM, T, window, tb, te);
+    c[q] = te - tb + 1;
+    total += c[q];
+  }
+  static std::mutex mu;
+  static std::map<std::pair<std::vector<int>, int>, std::pair<int, std::vector<std::vector<int>>>>
+      cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(c, R);
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    std::vector<std::vector<int>> sig;
+    const int mx = balance_rounds(c, R, sig);
+    it = cache.emplace(key, std::make_pair(mx, std::move(sig))).first;
+  }
+  const int mx = it->second.first;
+  if ((int64_t)mx * nqt * 100 > (int64_t)108 * R * total) return ord;  // above 1.08 x the mean
+  ord.rounds = R;
+  ord.nqt = nqt;
+  ord.per_round = per_round;
+  for (int k = 0; k < R; ++k)
+    for (int q = 0; q < nqt; ++q) {
+      const int e = k * nqt + q;
+      ord.q4[e >> 2] |= (unsigned)it->second.second[k][q] << (8 * (e & 3));
+    }
+  return ord;
+}
+
 // Launch arguments shared by the entry points.
 struct Bf16Args {
   const void *q, *k, *v;
@@ -1148,10 +1321,11 @@ static hipError_t launch_bf16_t(const Bf16Args& a, hipStream_t stream) {
     hipError_t e = resident_workgroups<Tag>(attn_fwd_bf16_stream<D, MODE, QKN, KN>, &resident);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(n_items < resident ? n_items : resident);
+    const ItemOrder ord = item_order<D, MODE>((int)grid, BH, a.T, a.window, nqt);
     hipLaunchKernelGGL((attn_fwd_bf16_stream<D, MODE, QKN, KN>), dim3(grid), dim3(256), 0, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse,
                        a.cos_tab, a.sin_tab, a.eps, a.geo, make_fastdiv((uint32_t)BH), a.T,
-                       a.window, scale_log2, nqt);
+                       a.window, scale_log2, nqt, ord);
   } else {
     static_assert(!KN, "keys are normalised in the kernel only by the streaming kernel (d <= 64)");
     hipLaunchKernelGGL((attn_fwd_bf16_tile<D, MODE, QKN>), dim3((unsigned)n_items), dim3(256), 0,
