@@ -185,9 +185,10 @@ int attn_fwd_qnorm(const void* q, const void* k, const void* v, void* out, float
  * Rounding differs from attn_qknorm_rope + attn_fwd in one place: q's normalised, rotated row is
  * multiplied by log2(e)/sqrt(d) in fp32 before its one rounding to bf16. With k_work NULL the
  * keys' rotation angles are also formed in the kernel in fp32 (t times the frequency that row 1
- * of the tables gives, reduced to one turn), which moves a rotated key by up to about 2e-4 of its
- * norm against the table's angles for T below 8192, and a key row's RMS uses the hardware
- * reciprocal square root (about 1 ulp) before the row's one rounding to bf16.
+ * of the tables gives, reduced to one turn; at d = 64 consecutive key tiles advance the previous
+ * tile's cos and sin by the rotation of 64 positions), which moves a rotated key by up to about
+ * 2e-4 of its norm against the table's angles for T below 8192, and a key row's RMS uses the
+ * hardware reciprocal square root (about 1 ulp) before the row's one rounding to bf16.
  */
 int attn_fwd_qknorm(const void* q, const void* k, const void* v, void* k_work, void* out,
                     float* lse, const float* cos_tab, const float* sin_tab, int B, int H, int T,

@@ -620,9 +620,13 @@ struct ItemOrder {
 // no separate k pass, no normalised k written). A tile is normalised by every item that streams
 // it. The rotation angles are formed in the kernel: the lane's frequencies w_j (radians per
 // position) come from row 1 of the rotation tables as atan2(sin w_j, cos w_j), and the angle of
-// position t is t w_j reduced to one turn in fp32 before __sinf / __cosf, so the rotated rows
-// differ from the k pass's (fp64 table) by the fp32 error of t w_j (below 2e-4 rad for t < 2^13);
-// the row's RMS uses v_rsq_f32 (about 1 ulp) where the k pass divides by a square root.
+// position t is t w_j reduced to one turn in fp32 before v_sin_f32 / v_cos_f32, so the rotated
+// rows differ from the k pass's (fp64 table) by the fp32 error of t w_j (below 2e-4 rad for
+// t < 2^13). At d = 64 a tile that follows the previous one (64 positions on, the common case
+// inside an item) instead advances each lane's cos and sin by the rotation of 64 w_j, four fp32
+// operations per frequency in place of a sine and a cosine; each step adds a few ulps, and a
+// run restarts from the direct form at every item. The row's RMS uses v_rsq_f32 (about 1 ulp)
+// where the k pass divides by a square root.
 // ---------------------------------------------------------------------------------------------
 template <int D, int MODE, bool QKN, bool KN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
@@ -654,7 +658,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
   // p + 4 (their rotation partners, d/2 further); at d = 32 the partner chunk p ^ 2 sits in lane
   // p ^ 2. kfr[i]: turns per position of the lane's frequency index 8 (p % (CH / 2)) + i.
   constexpr int KCH = C::CH;  // 16-byte chunks per row
-  float kfr[8];
+  // kcs, ksn: cos and sin of the lane's row angles for the tile normalised last (first key at
+  // key_t0, wave-uniform); kc64, ks64: cos and sin of 64 w, the step to the next tile of a run.
+  // (d = 64 only: at d = 32 the 32 extra registers would cost the third workgroup per compute
+  // unit, so every tile forms its angles afresh.)
+  constexpr bool KINC = D >= 64;
+  float kfr[8], kcs[8], ksn[8], kc64[8], ks64[8];
+  int key_t0 = -2 * C::BN;
   if constexpr (KN) {
     static_assert(C::LPT * 64 / C::CH == 16, "a wave's direct loads of a K tile are its 16 rows");
     const int p = w.lane & 3;
@@ -664,6 +674,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
       const float c1 = T > 1 ? cos_tab[D / 2 + j0 + i] : 1.f;
       const float s1 = T > 1 ? sin_tab[D / 2 + j0 + i] : 0.f;
       kfr[i] = atan2f(s1, c1) * 0.15915494309189535f;  // 1 / (2 pi)
+      float turns = (float)C::BN * kfr[i];
+      turns -= rintf(turns);
+      kc64[i] = __builtin_amdgcn_cosf(turns);
+      ks64[i] = __builtin_amdgcn_sinf(turns);
+      kcs[i] = 1.f;
+      ksn[i] = 0.f;
     }
     // formed before the first direct load is issued, so their wait waits for nothing else
     asm volatile("" : "+v"(kfr[0]), "+v"(kfr[1]), "+v"(kfr[2]), "+v"(kfr[3]), "+v"(kfr[4]),
@@ -678,16 +694,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
     const int r = 16 * w.wave + (ln >> 2), p = ln & 3;
     const int sw = swz_k<D>(r);
     char* row = smem + st * (2 * C::TILE_BYTES) + r * C::ROW_BYTES;
-    const float tpos = (float)(t0 + r);
-    float cs[8], sn[8];
+    if (KINC && t0 == key_t0 + C::BN) {
+      // the next tile of a run of consecutive tiles: the angles advance by 64 w
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // v_sin_f32 / v_cos_f32 take the angle in turns; reduced to [-1/2, 1/2] first
-      float turns = tpos * kfr[i];
-      turns -= rintf(turns);
-      cs[i] = __builtin_amdgcn_cosf(turns);
-      sn[i] = __builtin_amdgcn_sinf(turns);
+      for (int i = 0; i < 8; ++i) {
+        const float c = kcs[i], sv = ksn[i];
+        kcs[i] = fmaf(c, kc64[i], -(sv * ks64[i]));
+        ksn[i] = fmaf(sv, kc64[i], c * ks64[i]);
+      }
+    } else {
+      const float tpos = (float)(t0 + r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // v_sin_f32 / v_cos_f32 take the angle in turns; reduced to [-1/2, 1/2] first
+        float turns = tpos * kfr[i];
+        turns -= rintf(turns);
+        kcs[i] = __builtin_amdgcn_cosf(turns);
+        ksn[i] = __builtin_amdgcn_sinf(turns);
+      }
     }
+    key_t0 = t0;
+    const float(&cs)[8] = kcs;
+    const float(&sn)[8] = ksn;
     // sums over the row's four lanes (lanes 4 m .. 4 m + 3, a DPP quad)
     auto quad_sum = [](float x) {
       x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1,
