@@ -144,6 +144,34 @@ def test_fused_layer_parity_full_size_sampled(index):
         del out, lse
 
 
+
+@pytest.mark.parametrize("d,window", [(64, 512), (64, -1), (32, 512), (32, -1)])
+@pytest.mark.parametrize("write_k", [True, False])
+def test_head_grouped_order_ragged(d, window, write_k):
+    """192 heads with a ragged length (T = 1000, eight query blocks, the last one partial): the
+    launch takes the head-grouped item order (whole rounds of heads, per-round block
+    permutations) at d = 64 with either mask and at d = 32 causal, and the snake order at d = 32
+    with W = 512 (two rounds cannot balance that mask's blocks within 8 %). Every output must be
+    written (they start as NaN) and sampled rows of sampled heads match the oracle, with the keys
+    normalised by the k pass or inside the kernel."""
+    B, H, T = 16, 12, 1000
+    say(f"head-grouped order ragged d={d} W={window} write_k={write_k}")
+    q, k, v = (inputs.make_random((B, H, T, d), torch.bfloat16, s) for s in (301, 302, 303))
+    cos, sin = ops.rope_table(T, d)
+    out0 = torch.full((B, H, T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse0 = torch.full((B, H, T), float("nan"), dtype=torch.float32, device="cuda")
+    out, lse, _ = ops.attn_fwd_qknorm(dev(q), dev(k), dev(v), cos, sin, window=window,
+                                      out=out0, lse=lse0, write_k=write_k)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(7)
+    rows = np.array(sorted({0, 1, 127, 128, 895, 896, 999} |
+                           set(int(x) for x in rng.choice(T, 24, replace=False))))
+    for b, h in ((0, 0), (B - 1, H - 1), (5, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        check(out[sl].cpu(), lse[sl].cpu(), q[sl], k[sl], v[sl], window, rows=rows)
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 def test_fused_matches_two_call_path_and_k_work(d):
     """k_work equals attn_qknorm_rope's k output bitwise; out and lse stay within the bf16
