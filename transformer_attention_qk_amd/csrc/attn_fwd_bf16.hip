@@ -624,9 +624,9 @@ struct ItemOrder {
 // rows differ from the k pass's (fp64 table) by the fp32 error of t w_j (below 2e-4 rad for
 // t < 2^13). At d = 64 a tile that follows the previous one (64 positions on, the common case
 // inside an item) instead advances each lane's cos and sin by the rotation of 64 w_j, four fp32
-// operations per frequency in place of a sine and a cosine; each step adds a few ulps, and a
-// run restarts from the direct form at every item. The row's RMS uses v_rsq_f32 (about 1 ulp)
-// where the k pass divides by a square root.
+// operations per frequency in place of a sine and a cosine; each step adds a few ulps, and the
+// direct form restarts the run wherever the stream jumps (a new item). The row's RMS uses
+// v_rsq_f32 (about 1 ulp) where the k pass divides by a square root.
 // ---------------------------------------------------------------------------------------------
 template <int D, int MODE, bool QKN, bool KN>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_stream(
@@ -1186,12 +1186,8 @@ static hipError_t resident_workgroups(Kern kern, int* out) {
   return hipSuccess;
 }
 
-// Per-round permutations sig[k] of the n query blocks over the n workgroups of a head's group
-// (block costs c, in tiles plus one for the transition, in rank order), so that the workgroups'
-// summed costs stay close to their mean. Rounds alternate the identity and the reverse (which
-// pairs heavy with light blocks); an odd count of three or more starts with the best triple
-// (sig 1 over every permutation when n <= 8, sig 2 by bottleneck matching); single swaps within
-// a round that lower the largest sum finish it. Returns the largest sum.
+// A permutation perm (slot -> block) with base[s] + c[perm[s]] <= cap for every slot s, if one
+// exists (bipartite matching by augmenting paths; n is at most a few dozen).
 static bool match_under(const std::vector<int>& base, const std::vector<int>& c, int cap,
                         std::vector<int>& perm) {
   const int n = (int)c.size();
@@ -1217,6 +1213,12 @@ static bool match_under(const std::vector<int>& base, const std::vector<int>& c,
   return true;
 }
 
+// Per-round permutations sig[k] of the n query blocks over the n workgroups of a head's group
+// (block costs c, in tiles plus one for the transition, in rank order), so that the workgroups'
+// summed costs stay close to their mean. Rounds alternate the identity and the reverse (which
+// pairs heavy with light blocks); an odd count of three or more starts with the best triple
+// (sig 1 over every permutation when n <= 8, sig 2 by bottleneck matching); single swaps within
+// a round that lower the largest sum finish it. Returns the largest sum.
 static int balance_rounds(const std::vector<int>& c, int R, std::vector<std::vector<int>>& sig) {
   const int n = (int)c.size();
   sig.assign(R, std::vector<int>(n));
