@@ -24,6 +24,9 @@ the k-only prologue launch also gates v) against the plain layer call, and the g
 
 The line's "cache_states" object times the attention launch alone in two more cache states:
 hot (one layer's launch repeated back to back) and cold (a 512 MiB write before each launch).
+The "item_order" object times the attention launches in the default item order and in the snake
+order (ATTN_ITEM_ORDER=snake), alternating step by step, in-model and cold, and checks that the
+outputs are bitwise the same.
 
 --workload autoresearch_default times the train.py listing's default model instead (B=128, H=4,
 T=2048, d=128, eight layers "SSSL" with windows 1024 / 2048) on q, k, v in the projections'
@@ -495,11 +498,54 @@ def main() -> int:
     # before each launch. The in-model order above (k just written by the prologue) is the
     # headline state.
     hot_ms = cold_ms = None
+    order_cmp = None
     if not args.no_cache_states:
         hot_ms = [time_alone(l) for l in range(L)]
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         cold_ms = [time_alone(l, lambda: flush.fill_(1)) for l in range(L)]
-        del flush
+        # The default item order against the snake order (ATTN_ITEM_ORDER=snake, read by the
+        # library at each call): outputs must match bitwise; then the two alternate step by step
+        # in one loop (each launch right after its layer's k pass, as in the model; and after a
+        # 512 MiB write, cold), so both see the same clocks and caches.
+        ref = [o.clone() for o in out] + [x.clone() for x in lse]
+
+        def attention_order(l, snake):
+            if snake:
+                os.environ["ATTN_ITEM_ORDER"] = "snake"
+            try:
+                return attention(l)
+            finally:
+                if snake:
+                    del os.environ["ATTN_ITEM_ORDER"]
+
+        for l in range(L):
+            _lib.check("attention (snake order)", attention_order(l, True))
+        torch.cuda.synchronize()
+        same = all(torch.equal(a_, b_) for a_, b_ in zip(ref, list(out) + list(lse)))
+
+        def time_orders(before) -> list[list[float]]:
+            evo = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+                    for _ in range(L)] for _ in range(2 * args.steps)]
+            torch.cuda.synchronize()
+            for s_ in range(2 * args.steps):
+                for l in range(L):
+                    before(l)
+                    a_, b_ = evo[s_][l]
+                    a_.record()
+                    attention_order(l, s_ % 2 == 1)
+                    b_.record()
+            torch.cuda.synchronize()
+            ms = [[0.0] * L, [0.0] * L]
+            for s_ in range(2 * args.steps):
+                for l in range(L):
+                    a_, b_ = evo[s_][l]
+                    ms[s_ % 2][l] += a_.elapsed_time(b_) / args.steps
+            return ms
+
+        order_model = time_orders(kprologue)
+        order_cold = time_orders(lambda l: flush.fill_(1))
+        order_cmp = (same, order_model, order_cold)
+        del flush, ref
     # A plain device copy of the k-only prologue's bytes (one k tensor read, one written), the
     # rate an HBM-bound read-and-write pass reaches on this part, beside the prologue's.
     copy_src = k[0].clone()
@@ -677,6 +723,22 @@ def main() -> int:
             "prologue_avg_launch_us": round(1e3 * sum(pro_ms) / L, 3),
             "prologue_bytes_per_launch": pro_bytes,
             "prologue_gbs": round(pro_bytes * L / (sum(pro_ms) * 1e-3) / 1e9, 1),
+        }
+    if order_cmp is not None:
+        same, (m_def, m_snk), (c_def, c_snk) = order_cmp
+        tf = lambda ms: round(step_flops / (sum(ms) * 1e-3) / 1e12, 3)  # noqa: E731
+        result["item_order"] = {
+            "note": "the attention launches in the library's item order (head-grouped where the "
+                    "heads divide into whole rounds) and in the snake order "
+                    "(ATTN_ITEM_ORDER=snake), alternating step by step: in-model (after the "
+                    "layer's k pass) and cold (after a 512 MiB write)",
+            "outputs_equal": bool(same),
+            "default_tflops": tf(m_def),
+            "snake_tflops": tf(m_snk),
+            "default_launch_us": [round(1e3 * t, 3) for t in m_def],
+            "snake_launch_us": [round(1e3 * t, 3) for t in m_snk],
+            "default_cold_tflops": tf(c_def),
+            "snake_cold_tflops": tf(c_snk),
         }
     if kin_ms is not None:
         result["k_in_kernel"] = {

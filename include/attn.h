@@ -136,6 +136,10 @@ int attn_qknorm_rope(const void* q, const void* k, void* q_out, void* k_out,
  * bf16: q k^T and P v run on bf16 MFMA with fp32 accumulation; the softmax is fp32 and the
  * probabilities are rounded to bf16 (nearest even) before the P v product; out is rounded to
  * nearest even. f32: every step in fp32.
+ * Results do not depend on the order in which the kernels take (head, query block) items: the
+ * environment variable ATTN_ITEM_ORDER=snake (read at each call) replaces the bf16 d <= 64
+ * kernels' head-grouped order with the snake order, for comparison, with bitwise the same
+ * outputs.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int T, int d, int window, int causal, int dtype, void* stream);

@@ -49,6 +49,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
+#include <cstring>
 #include <functional>
 #include <map>
 #include <mutex>
@@ -1286,9 +1288,13 @@ static int balance_rounds(const std::vector<int>& c, int R, std::vector<std::vec
 // The head-grouped order for a launch of P workgroups, or rounds = 0 (the snake order) when the
 // shape does not divide into whole rounds, the table does not fit, or the best permutations found
 // leave a workgroup more than 8 % above the mean. Permutations are kept per (costs, rounds).
+// ATTN_ITEM_ORDER=snake in the environment (read at each launch) keeps the snake order, for
+// comparing the two; outputs are bitwise the same either way.
 template <int D, int MODE>
 static ItemOrder item_order(int P, int BH, int T, int window, int nqt) {
   ItemOrder ord{};
+  const char* env = std::getenv("ATTN_ITEM_ORDER");
+  if (env != nullptr && std::strcmp(env, "snake") == 0) return ord;
   if (P % 8 != 0 || BH % 8 != 0 || nqt < 1 || nqt > 255) return ord;
   const int J = P / 8, hpc = BH / 8;
   if (J % nqt != 0) return ord;
