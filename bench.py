@@ -42,6 +42,10 @@ Extra modes (used to collect rocprofv3 counters; they print no JSON):
   --dma-calibration      run the attention kernel where it reads every byte once (non-causal,
                          T = 128: one query block per head, each K/V tile read by one item), so
                          the counters of its direct-to-LDS loads can be checked against known bytes
+  --issue-rates          run the issue-rate probe (libattn_diag.so, diag/issue_rates.hip): cycles
+                         per loop of independent MFMAs, exponentials, FMAs, packs, dot products
+                         and adds, alone and interleaved in one wave, with one and two waves per
+                         SIMD; prints a table
 """
 
 from __future__ import annotations
@@ -188,6 +192,33 @@ def cpu_baseline(w, layer_inputs, windows: list[int], workers: int) -> dict:
     }
 
 
+def issue_rates() -> int:
+    """Print the issue-rate probe's table (cycles per loop iteration, max over the waves)."""
+    import ctypes
+    from transformer_attention_qk_amd import build as _build
+    if not os.path.exists(_build.DIAG_PATH):
+        print(f"{_build.DIAG_PATH} is missing: build it with __graft_entry__.build()", file=sys.stderr)
+        return 1
+    lib = ctypes.CDLL(_build.DIAG_PATH)
+    lib.attn_diag_issue_name.restype = ctypes.c_char_p
+    lib.attn_diag_issue_name.argtypes = [ctypes.c_int]
+    lib.attn_diag_issue_rates.restype = ctypes.c_int
+    lib.attn_diag_issue_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    names = []
+    while lib.attn_diag_issue_name(len(names)) is not None:
+        names.append(lib.attn_diag_issue_name(len(names)).decode())
+    cyc = (ctypes.c_double * (2 * len(names)))()
+    rc = lib.attn_diag_issue_rates(cyc, 2 * len(names))
+    if rc != 0:
+        print(f"attn_diag_issue_rates failed with HIP error {rc}", file=sys.stderr)
+        return 1
+    print("| loop body (independent instructions) | 1 wave per SIMD | 2 waves per SIMD |")
+    print("|---|---|---|")
+    for m, name in enumerate(names):
+        print(f"| {name} | {cyc[2 * m]:.1f} | {cyc[2 * m + 1]:.1f} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +238,7 @@ def main() -> int:
                     choices=["attn", "kprologue", "attn_unfused", "prologue", "decode", "bwd"])
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--dma-calibration", action="store_true")
+    ap.add_argument("--issue-rates", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -223,7 +255,8 @@ def main() -> int:
     # The CPU baseline runs first, before anything touches the GPU, because its process pool
     # forks. Its inputs are the same seeded tensors the GPU step uses.
     cpu_result = None
-    if not (args.no_cpu_baseline or args.only or args.copy_calibration or args.dma_calibration):
+    if not (args.no_cpu_baseline or args.only or args.copy_calibration or args.dma_calibration
+            or args.issue_rates):
         names0 = [x.name for x in inputs.WORKLOADS] + [inputs.MODEL_DEFAULT.name]
         if args.workload in names0:
             import oracle
@@ -240,6 +273,9 @@ def main() -> int:
         return 1
     _lib.load()
     torch.cuda.set_device(0)
+
+    if args.issue_rates:
+        return issue_rates()
 
     if args.copy_calibration:
         n = 256 << 20

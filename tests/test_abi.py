@@ -712,3 +712,24 @@ def test_decode_noalloc_scratch_limit_matches_workspace_sizes(lib):
         _lib.ATTN_DECODE_SCRATCH_BYTES
     assert "scratch" in lib.attn_strerror(_lib.ATTN_ERR_SCRATCH).decode()
 
+
+
+def test_issue_rate_probe_loads_and_names_its_modes():
+    # The issue-rate probe behind bench.py --issue-rates is a library of its own; here it only
+    # loads and names its loops (no kernel runs).
+    from transformer_attention_qk_amd import build as _build
+    path = _build.DIAG_PATH if os.path.exists(_build.DIAG_PATH) else _build.build_diag_library()
+    d = ctypes.CDLL(path)
+    d.attn_diag_issue_name.restype = ctypes.c_char_p
+    d.attn_diag_issue_name.argtypes = [ctypes.c_int]
+    d.attn_diag_issue_rates.restype = ctypes.c_int
+    d.attn_diag_issue_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    names = []
+    while d.attn_diag_issue_name(len(names)) is not None:
+        names.append(d.attn_diag_issue_name(len(names)).decode())
+    assert len(names) == 9
+    assert names[0].startswith("16 mfma") and "v_dot2c_f32_bf16" in names[7]
+    assert d.attn_diag_issue_name(-1) is None
+    # too small an output array is refused before any HIP call
+    buf = (ctypes.c_double * 4)()
+    assert d.attn_diag_issue_rates(buf, 4) != 0

@@ -68,5 +68,28 @@ def build_library(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+DIAG_NAME = "libattn_diag.so"
+DIAG_PATH = os.path.join(PKG_DIR, DIAG_NAME)
+
+
+def build_diag_library(verbose: bool = False) -> str:
+    """Compile the issue-rate probe (diag/issue_rates.hip) into libattn_diag.so. It is a
+    measurement tool that bench.py --issue-rates loads; the attention library does not use it."""
+    src = os.path.join(PKG_DIR, "diag", "issue_rates.hip")
+    fd, tmp = tempfile.mkstemp(prefix=".libattn_diag.", suffix=".so.tmp", dir=PKG_DIR)
+    os.close(fd)
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in proc.stderr.splitlines() if "packed-fp32-ops" not in l).strip()
+    if proc.returncode != 0:
+        os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
+    os.replace(tmp, DIAG_PATH)
+    return DIAG_PATH
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_diag_library(verbose=True))
